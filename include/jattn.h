@@ -1,0 +1,179 @@
+/*
+ * jattn.h -- C ABI of libjattn.so: jagged (unpadded, variable-length)
+ * dot-product attention, forward and backward, for AMD MI355X (gfx950).
+ *
+ * What is computed.  "Training GEM at LLM scale" (Meta engineering post):
+ *   - section "Jagged Sequence Flash Attention": attention over jagged
+ *     tensors without padding, custom additive attention bias, query and
+ *     key/value lengths that differ per sample, and a backward pass;
+ *   - section "Generalized Dot-Product Attention (GDPA)": the same two
+ *     matrix products with GELU or SiLU applied element-wise in place of
+ *     softmax (no normalisation);
+ *   - section "BlockAttention": a fixed 64-token block-diagonal mask.
+ * For sample b and head h, with Q_b [lq,D], K_b, V_b [lk,D]:
+ *   S = scale * Q_b K_b^T + bias_b[h]
+ *   softmax:  P = softmax_row(S), O = P V, LSE_i = ln sum_j exp(S_ij)
+ *   GDPA:     P = act(S),        O = P V   (act = erf-GELU or SiLU)
+ *   block-diagonal: only pairs with floor(i/64) == floor(j/64) take part.
+ * There is no causal mask.  Zero-length samples: rows with lk = 0 get O = 0,
+ * LSE = -inf and dQ = 0; rows with lq = 0 get dK = dV = 0.  The library
+ * writes these zeros itself and never assumes zeroed output buffers.
+ *
+ * Layouts (device memory, row-major, caller-owned):
+ *   q, o, dout, dq     [Tq, H, D]   Tq = q_offsets[B]
+ *   k, v, dk, dv       [Tk, H, D]   Tk = kv_offsets[B]
+ *   lse                [Tq, H] float32 (softmax only)
+ *   bias, dbias        samples concatenated: sample b is [H, lq_b, lk_b]
+ *                      row-major at element offset sum_{j<b} H lq_j lk_j
+ *   offsets            host int64 [B+1], offsets[0] = 0, non-decreasing.
+ * Value pointers must be 16-byte aligned; bias/dbias 4-byte aligned.
+ *
+ * Ownership and threading.  The caller owns every device buffer, including
+ * the workspace (size from jattn_plan_info).  The library never allocates
+ * device memory.  A plan is host memory owned by the library, immutable
+ * after creation and safe to share between threads.  Work is enqueued on
+ * the given stream (a hipStream_t; NULL = the null stream) and the call
+ * returns without waiting; device faults surface at the caller's next
+ * synchronisation.  Two calls in flight must not share one workspace.
+ *
+ * Errors.  Every call returns JATTN_OK (0) or a negative JATTN_E_* code.
+ * Arguments are validated on the host before anything is enqueued; on
+ * error nothing is launched.  jattn_last_error() gives a text for the most
+ * recent failure on the calling thread.  Nothing is thrown across the ABI.
+ */
+#ifndef JATTN_H
+#define JATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define JATTN_OK 0
+#define JATTN_E_NULL (-1)        /* a required pointer is NULL */
+#define JATTN_E_OFFSETS (-2)     /* offsets[0] != 0, decreasing, or a total >= 2^31 rows */
+#define JATTN_E_SHAPE (-3)       /* bad B, H, D, or block-diagonal with lq != lk */
+#define JATTN_E_UNSUPPORTED (-4) /* unsupported dtype / activation / mask combination */
+#define JATTN_E_ALIGN (-5)       /* misaligned device pointer */
+#define JATTN_E_WORKSPACE (-6)   /* workspace missing or too small */
+#define JATTN_E_STATE (-7)       /* e.g. LSE missing for a softmax backward */
+#define JATTN_E_HIP (-8)         /* a HIP runtime call or launch failed */
+#define JATTN_E_ARG (-9)         /* other invalid argument */
+
+/* activation (desc.act) */
+#define JATTN_SOFTMAX 0
+#define JATTN_GELU_ERF 1 /* GDPA with x * Phi(x) */
+#define JATTN_SILU 2     /* GDPA with x * sigmoid(x) */
+
+/* mask (desc.mask) */
+#define JATTN_MASK_NONE 0
+#define JATTN_MASK_BLOCKDIAG64 1 /* BlockAttention, requires lq_b == lk_b */
+
+/* element types */
+#define JATTN_BF16 0
+#define JATTN_F32 1
+
+/* unit order across workers (desc.order) */
+#define JATTN_HEAVY_FIRST 0 /* cost-sorted units dealt round-robin */
+#define JATTN_ZIGZAG 1      /* cost-sorted units dealt boustrophedon */
+#define JATTN_LPT 2         /* cost-sorted units to the least-loaded worker */
+
+/* plan parts (jattn_plan_export "which") */
+#define JATTN_PLAN_FWD 0  /* forward units (b, h, q-tile) */
+#define JATTN_PLAN_DKDV 1 /* dK/dV units (b, h, kv-tile) */
+#define JATTN_PLAN_DQ 2   /* dQ units (b, h, q-tile) */
+#define JATTN_PLAN_BLOCK 3 /* block-diagonal units (b, h, 64-block) */
+
+typedef struct jattn_plan jattn_plan; /* opaque */
+
+typedef struct {
+  int32_t B, H, D;      /* D in {32, 64, 128}; H >= 1; B >= 0 */
+  float scale;          /* softmax/GDPA scale; <= 0 selects 1/sqrt(D) */
+  int32_t act;          /* JATTN_SOFTMAX | JATTN_GELU_ERF | JATTN_SILU */
+  int32_t mask;         /* JATTN_MASK_NONE | JATTN_MASK_BLOCKDIAG64 */
+  int32_t has_bias;     /* 0/1: additive bias input */
+  int32_t want_dbias;   /* 0/1: backward writes dBias (needs has_bias) */
+  int32_t in_dtype;     /* q, k, v, bias, dout: JATTN_BF16 | JATTN_F32 */
+  int32_t out_dtype;    /* o */
+  int32_t grad_dtype;   /* dq, dk, dv (dbias always uses in_dtype) */
+  int32_t split_operands; /* 0/1: P and dS enter the PV-type products as
+                             bf16 hi + lo pairs (two MFMAs) for accuracy */
+  int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
+  int32_t num_workers;  /* persistent workgroups per kernel; 0 = default */
+} jattn_desc;
+
+/* Per-kernel plan figures.  tile_rows: rows of the unit's own tile (q rows
+ * for fwd/dq, kv rows for dkdv, 64 for block); step_rows: rows consumed per
+ * inner-loop step (kv for fwd/dq, q for dkdv). */
+typedef struct {
+  int32_t tile_rows, step_rows, num_workers, n_units;
+} jattn_kernel_plan;
+
+typedef struct {
+  int64_t workspace_bytes; /* device workspace needed by fwd and bwd */
+  int64_t Tq, Tk;          /* total query / key rows */
+  int64_t bias_elems;      /* sum_b H lq_b lk_b */
+  double flops_fwd;        /* algorithmic: 4 H D sum(lq lk) (allowed pairs) */
+  double flops_bwd;        /* 2.5 x flops_fwd */
+  jattn_kernel_plan fwd, dkdv, dq, block;
+} jattn_plan_summary;
+
+/* Build a plan on the host from host offset arrays (int64 [B+1] each).
+ * Validates offsets and the descriptor, enumerates the valid tiles of every
+ * kernel and orders them across workers ("Training GEM at LLM scale",
+ * section "Generalized Dot-Product Attention (GDPA)": valid tiles are
+ * precomputed on the CPU, empty ones skipped, and assigned in zigzag order).
+ * On success *out owns the plan (free with jattn_plan_destroy).  Touches no
+ * GPU. */
+int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets,
+                      const int64_t* kv_offsets, jattn_plan** out);
+
+/* Fill *summary.  Host only. */
+int jattn_plan_info(const jattn_plan* plan, jattn_plan_summary* summary);
+
+/* Copy a plan part to host memory as int32.  which = JATTN_PLAN_* * 2 + part,
+ * part 0 = units as (b, h, tile, cost) quadruples in worker order,
+ * part 1 = worker offsets [num_workers + 1].  *n receives the number of
+ * int32 written (or needed, when dst is NULL).  Host only. */
+int jattn_plan_export(const jattn_plan* plan, int32_t which, int32_t* dst, int64_t cap,
+                      int64_t* n);
+
+/* Enqueue a copy of the plan into the caller's device workspace.  Must be
+ * done once per (plan, workspace) pair before jattn_fwd / jattn_bwd use that
+ * workspace; the plan region is never modified by fwd/bwd. */
+int jattn_plan_upload(const jattn_plan* plan, void* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/* Forward.  Writes o (out_dtype) and, for softmax with mask NONE, lse.
+ * bias: required iff desc.has_bias.  lse may be NULL (not written) for
+ * softmax; it must be NULL-or-ignored for GDPA and block mode, which keep
+ * no row statistics ("BlockAttention" section: no logsumexp traffic). */
+int jattn_fwd(const jattn_plan* plan, const void* q, const void* k, const void* v,
+              const void* bias, void* o, float* lse, void* workspace, void* stream);
+
+/* Backward.  Given dout, writes dq, dk, dv (grad_dtype) and, if
+ * desc.want_dbias, dbias (in_dtype).  Softmax with mask NONE needs o and
+ * the forward's lse (JATTN_E_STATE otherwise); GDPA needs neither; block
+ * mode recomputes its row statistics in-tile and needs neither.  Uses the
+ * workspace's scratch region for row statistics.  No atomics: every output
+ * element has exactly one writer, so results are run-to-run identical
+ * ("Jagged Sequence Flash Attention" section: separate dQ pass, no atomic
+ * adds). */
+int jattn_bwd(const jattn_plan* plan, const void* q, const void* k, const void* v,
+              const void* bias, const void* o, const float* lse, const void* dout, void* dq,
+              void* dk, void* dv, void* dbias, void* workspace, void* stream);
+
+void jattn_plan_destroy(jattn_plan* plan);
+
+/* Static text for a status code. */
+const char* jattn_strerror(int status);
+
+/* Detail of the calling thread's most recent failure ("" if none). */
+const char* jattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JATTN_H */

@@ -1,0 +1,116 @@
+"""Torch-facing helper around the C ABI: owns a plan and its device workspace,
+allocates outputs, and passes raw pointers plus the current HIP stream.
+PyTorch supplies memory and streams only; all computation is in libjattn.so.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as _b
+
+_ACT = {"softmax": _b.JATTN_SOFTMAX, "gelu": _b.JATTN_GELU_ERF, "silu": _b.JATTN_SILU}
+_DT = {"bf16": _b.JATTN_BF16, "f32": _b.JATTN_F32}
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+_ORDER = {"heavy_first": _b.JATTN_HEAVY_FIRST, "zigzag": _b.JATTN_ZIGZAG, "lpt": _b.JATTN_LPT}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+class JaggedAttention:
+    """One jagged batch layout (offsets + options) bound to a plan."""
+
+    def __init__(self, q_offsets, kv_offsets, H: int, D: int, *, act: str = "softmax",
+                 block_diagonal: bool = False, has_bias: bool = False, want_dbias: bool = False,
+                 in_dtype: str = "bf16", out_dtype: Optional[str] = None,
+                 grad_dtype: Optional[str] = None, split_operands: bool = False,
+                 order: str = "heavy_first", num_workers: int = 0, scale: Optional[float] = None,
+                 device="cuda"):
+        q_offsets = np.asarray(q_offsets, dtype=np.int64)
+        kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
+        self.B = len(q_offsets) - 1
+        self.H, self.D = H, D
+        self.act = act
+        self.in_dtype = in_dtype
+        self.out_dtype = out_dtype or in_dtype
+        self.grad_dtype = grad_dtype or in_dtype
+        self.has_bias, self.want_dbias = has_bias, want_dbias
+        self.block_diagonal = block_diagonal
+        self.scale = (1.0 / math.sqrt(D)) if scale is None else scale
+        self.device = torch.device(device)
+        d = _b.jattn_desc()
+        d.B, d.H, d.D, d.scale = self.B, H, D, self.scale
+        d.act = _ACT[act]
+        d.mask = _b.JATTN_MASK_BLOCKDIAG64 if block_diagonal else _b.JATTN_MASK_NONE
+        d.has_bias, d.want_dbias = int(has_bias), int(want_dbias)
+        d.in_dtype, d.out_dtype, d.grad_dtype = _DT[in_dtype], _DT[self.out_dtype], _DT[self.grad_dtype]
+        d.split_operands = int(split_operands)
+        d.order = _ORDER[order]
+        d.num_workers = num_workers
+        self.desc = d
+        self.plan = _b.jattn_plan_create(d, q_offsets, kv_offsets)
+        self.info = _b.jattn_plan_info(self.plan)
+        self.Tq, self.Tk = int(self.info.Tq), int(self.info.Tk)
+        self.workspace = None
+
+    def upload(self, stream=None):
+        """Allocate the workspace on the device and copy the plan into it."""
+        nbytes = int(self.info.workspace_bytes)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device).cuda_stream
+        _b.jattn_plan_upload(self.plan, self.workspace.data_ptr(), self.workspace.numel(), st)
+        return self
+
+    def _stream(self):
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def forward(self, q, k, v, bias=None, o=None, lse=None, want_lse=True):
+        if self.workspace is None:
+            self.upload()
+        if o is None:
+            o = torch.empty(self.Tq, self.H, self.D, dtype=_TORCH_DT[self.out_dtype], device=self.device)
+        if lse is None and want_lse and self.act == "softmax" and not self.block_diagonal:
+            lse = torch.empty(self.Tq, self.H, dtype=torch.float32, device=self.device)
+        _b.jattn_fwd(self.plan, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse),
+                     self.workspace.data_ptr(), self._stream())
+        return o, lse
+
+    def backward(self, q, k, v, dout, o=None, lse=None, bias=None, dq=None, dk=None, dv=None, dbias=None):
+        if self.workspace is None:
+            self.upload()
+        gdt = _TORCH_DT[self.grad_dtype]
+        dq = dq if dq is not None else torch.empty(self.Tq, self.H, self.D, dtype=gdt, device=self.device)
+        dk = dk if dk is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
+        dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
+        if self.want_dbias and dbias is None:
+            dbias = torch.empty(int(self.info.bias_elems), dtype=_TORCH_DT[self.in_dtype], device=self.device)
+        _b.jattn_bwd(self.plan, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout),
+                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
+        return dq, dk, dv, dbias
+
+    def __del__(self):
+        try:
+            _b.jattn_plan_destroy(self.plan)
+        except Exception:
+            pass
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host array from inputs.py (bf16 bits or float32) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> exact float64 numpy array."""
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,90 @@
+"""Build libjattn.so (HIP kernels for gfx950 + host planner/C ABI) in-tree.
+
+    python -m jagged_variable_length_amd.build [--incremental] [-j N]
+
+Every kernel translation unit is compiled with hipcc for gfx950 only; the
+result is jagged_variable_length_amd/libjattn.so.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libjattn.so")
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result"]
+
+# (source, object name, extra defines)
+FWD_INST = [(128, "bf16", "bf16"), (128, "bf16", "f32"), (64, "bf16", "bf16"), (64, "bf16", "f32"),
+            (64, "f32", "f32"), (32, "bf16", "bf16"), (32, "bf16", "f32"), (32, "f32", "f32")]
+
+
+def units():
+    u = [("api.cpp", "api", []), ("planner.cpp", "planner", [])]
+    for d, ti, to in FWD_INST:
+        u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
+    return u
+
+
+def _deps():
+    return [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "jattn.h")]
+
+
+def _compile(src, name, defs, incremental):
+    out = os.path.join(OBJ, name + ".o")
+    if incremental and os.path.exists(out):
+        newest = max(os.path.getmtime(p) for p in _deps())
+        if os.path.getmtime(out) >= newest:
+            return out, None
+    xflags = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [HIPCC] + FLAGS + defs + xflags + ["-c", os.path.join(CSRC, src), "-o", out]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (p.stdout + p.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{errs}")
+    return out, errs.strip() or None
+
+
+def build(incremental: bool = False, jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    objs = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_compile, s, n, d, incremental) for s, n, d in units()]
+        for f in futs:
+            o, msg = f.result()
+            objs.append(o)
+            if msg and verbose:
+                print(msg, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}{p.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--incremental", action="store_true")
+    ap.add_argument("-j", type=int, default=None)
+    ap.add_argument("-v", action="store_true")
+    a = ap.parse_args()
+    print(build(a.incremental, a.j, a.v))
+
+
+if __name__ == "__main__":
+    main()

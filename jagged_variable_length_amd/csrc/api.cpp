@@ -1,0 +1,343 @@
+// C ABI of libjattn.so: validation, planning, workspace layout and launches.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/jattn.h"
+#include "kernels.hpp"
+#include "planner.hpp"
+
+using jattn::KernelSel;
+using jattn::UnitList;
+
+struct jattn_plan {
+  jattn_desc desc;
+  float scale = 0.f;
+  int B = 0, H = 0, D = 0;
+  int64_t Tq = 0, Tk = 0, bias_elems = 0;
+  double pairs = 0.0;  // allowed (i, j) pairs summed over samples (per head)
+  int fwd_wq = 4, dq_wq = 4, dkdv_wkv = 4;
+  UnitList fwd, dkdv, dq, block;
+  std::vector<int32_t> image;  // uploaded plan (int32 words)
+  int64_t off_samples = 0, off_fwd_u = 0, off_fwd_o = 0, off_dkdv_u = 0, off_dkdv_o = 0;
+  int64_t off_dq_u = 0, off_dq_o = 0, off_blk_u = 0, off_blk_o = 0;  // in int32 words
+  int64_t plan_bytes = 0, di_off = 0, workspace_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return JATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kDefaultWorkers = 256;  // one persistent workgroup per CU
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Append a unit list to the image, 16-byte aligned sections.
+void append(std::vector<int32_t>& img, const UnitList& L, int64_t* off_u, int64_t* off_o) {
+  img.resize((size_t)align_up((int64_t)img.size(), 4), 0);
+  *off_u = (int64_t)img.size();
+  img.insert(img.end(), L.units.begin(), L.units.end());
+  img.resize((size_t)align_up((int64_t)img.size(), 4), 0);
+  *off_o = (int64_t)img.size();
+  img.insert(img.end(), L.offsets.begin(), L.offsets.end());
+}
+
+int elem_size(int dt) { return dt == JATTN_F32 ? 4 : 2; }
+
+KernelSel base_sel(const jattn_plan* p) {
+  KernelSel k{};
+  k.D = p->D;
+  k.act = p->desc.act;
+  k.bias = p->desc.has_bias != 0;
+  k.dbias = p->desc.want_dbias != 0;
+  k.split = p->desc.split_operands != 0;
+  k.in_f32 = p->desc.in_dtype == JATTN_F32;
+  return k;
+}
+
+const int32_t* ws_ptr(void* ws, int64_t off_words) {
+  return reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + off_words * 4);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(JATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jattn_strerror(int status) {
+  switch (status) {
+    case JATTN_OK: return "ok";
+    case JATTN_E_NULL: return "null pointer";
+    case JATTN_E_OFFSETS: return "invalid offsets";
+    case JATTN_E_SHAPE: return "invalid shape";
+    case JATTN_E_UNSUPPORTED: return "unsupported combination";
+    case JATTN_E_ALIGN: return "misaligned pointer";
+    case JATTN_E_WORKSPACE: return "workspace missing or too small";
+    case JATTN_E_STATE: return "missing state";
+    case JATTN_E_HIP: return "HIP runtime error";
+    case JATTN_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* jattn_last_error(void) { return g_last_error.c_str(); }
+
+int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const int64_t* kv_offsets,
+                      jattn_plan** out) {
+  if (!desc || !q_offsets || !kv_offsets || !out) return fail(JATTN_E_NULL, "null argument to jattn_plan_create");
+  *out = nullptr;
+  const jattn_desc& d = *desc;
+  if (d.B < 0) return fail(JATTN_E_SHAPE, "B must be >= 0");
+  if (d.H < 1 || d.H > 4096) return fail(JATTN_E_SHAPE, "H must be in [1, 4096]");
+  if (d.D != 32 && d.D != 64 && d.D != 128) return fail(JATTN_E_SHAPE, "D must be 32, 64 or 128");
+  if (d.act < JATTN_SOFTMAX || d.act > JATTN_SILU) return fail(JATTN_E_UNSUPPORTED, "unknown activation");
+  if (d.mask != JATTN_MASK_NONE && d.mask != JATTN_MASK_BLOCKDIAG64)
+    return fail(JATTN_E_UNSUPPORTED, "unknown mask");
+  if (d.in_dtype != JATTN_BF16 && d.in_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown in_dtype");
+  if (d.out_dtype != JATTN_BF16 && d.out_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown out_dtype");
+  if (d.grad_dtype != JATTN_BF16 && d.grad_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown grad_dtype");
+  if (d.in_dtype == JATTN_F32 && (d.out_dtype != JATTN_F32 || d.grad_dtype != JATTN_F32))
+    return fail(JATTN_E_UNSUPPORTED, "fp32 inputs need fp32 outputs and gradients");
+  if (d.in_dtype == JATTN_F32 && d.D > 64) return fail(JATTN_E_UNSUPPORTED, "fp32 inputs support D <= 64");
+  if (d.want_dbias && !d.has_bias) return fail(JATTN_E_ARG, "want_dbias needs has_bias");
+  if (d.has_bias != 0 && d.has_bias != 1) return fail(JATTN_E_ARG, "has_bias must be 0 or 1");
+  if (d.mask == JATTN_MASK_BLOCKDIAG64 && (d.act != JATTN_SOFTMAX || d.has_bias))
+    return fail(JATTN_E_UNSUPPORTED, "block-diagonal mode supports softmax without bias");
+  if (d.order < JATTN_HEAVY_FIRST || d.order > JATTN_LPT) return fail(JATTN_E_ARG, "unknown order");
+  if (d.num_workers < 0 || d.num_workers > 65536) return fail(JATTN_E_ARG, "num_workers out of range");
+  if (!(d.scale == d.scale) || isinf(d.scale)) return fail(JATTN_E_ARG, "scale must be finite");
+
+  // offsets
+  const int B = d.B;
+  if (q_offsets[0] != 0 || kv_offsets[0] != 0) return fail(JATTN_E_OFFSETS, "offsets[0] must be 0");
+  std::vector<int32_t> lq(B), lk(B);
+  const int es = elem_size(d.in_dtype);
+  const int64_t row_bytes = (int64_t)d.H * d.D * es;
+  for (int b = 0; b < B; ++b) {
+    const int64_t a = q_offsets[b + 1] - q_offsets[b];
+    const int64_t c = kv_offsets[b + 1] - kv_offsets[b];
+    if (a < 0 || c < 0) return fail(JATTN_E_OFFSETS, "offsets must be non-decreasing");
+    if (q_offsets[b + 1] >= (int64_t(1) << 31) || kv_offsets[b + 1] >= (int64_t(1) << 31))
+      return fail(JATTN_E_OFFSETS, "total rows must be < 2^31");
+    if (a * row_bytes >= (int64_t(1) << 31) || c * row_bytes >= (int64_t(1) << 31))
+      return fail(JATTN_E_SHAPE, "one sample must span < 2^31 bytes");
+    if (d.has_bias && a * c * es >= (int64_t(1) << 31))
+      return fail(JATTN_E_SHAPE, "one sample's bias block per head must span < 2^31 bytes");
+    if (d.mask == JATTN_MASK_BLOCKDIAG64 && a != c)
+      return fail(JATTN_E_SHAPE, "block-diagonal mode needs lq == lk for every sample");
+    lq[b] = (int32_t)a;
+    lk[b] = (int32_t)c;
+  }
+
+  jattn_plan* p = new (std::nothrow) jattn_plan();
+  if (!p) return fail(JATTN_E_ARG, "out of host memory");
+  p->desc = d;
+  p->B = B;
+  p->H = d.H;
+  p->D = d.D;
+  p->scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.D);
+  p->Tq = q_offsets[B];
+  p->Tk = kv_offsets[B];
+
+  // sample table and algorithmic size
+  p->image.assign((size_t)8 * B, 0);
+  int64_t bias0 = 0;
+  int64_t sum_lq = 0, n_q = 0, sum_lk = 0, n_k = 0;
+  for (int b = 0; b < B; ++b) {
+    int32_t* s = &p->image[(size_t)8 * b];
+    s[0] = (int32_t)q_offsets[b];
+    s[1] = lq[b];
+    s[2] = (int32_t)kv_offsets[b];
+    s[3] = lk[b];
+    s[4] = (int32_t)(uint32_t)(bias0 & 0xffffffffLL);
+    s[5] = (int32_t)(bias0 >> 32);
+    bias0 += (int64_t)d.H * lq[b] * lk[b];
+    if (d.mask == JATTN_MASK_BLOCKDIAG64) {
+      for (int s0 = 0; s0 < lq[b]; s0 += 64) {
+        const double r = std::min(64, lq[b] - s0);
+        p->pairs += r * r;
+      }
+    } else {
+      p->pairs += (double)lq[b] * (double)lk[b];
+    }
+    if (lq[b] > 0) { sum_lq += lq[b]; ++n_q; }
+    if (lk[b] > 0) { sum_lk += lk[b]; ++n_k; }
+  }
+  p->bias_elems = bias0;
+  p->off_samples = 0;
+
+  const int W = d.num_workers > 0 ? d.num_workers : kDefaultWorkers;
+  const jattn::Order order = (jattn::Order)d.order;
+  if (d.mask == JATTN_MASK_BLOCKDIAG64) {
+    jattn::plan_units(jattn::kKindBlock, lq, lk, d.H, 64, 64, W, order, &p->block);
+  } else {
+    // Query-tile shape: 4 waves x 32 rows, or (short queries) one 32-row
+    // group whose key tiles are split over the 4 waves.
+    p->fwd_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
+    p->dq_wq = p->fwd_wq;
+    const int fwd_tile = 32 * p->fwd_wq, fwd_step = p->fwd_wq == 4 ? 64 : 128;
+    // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
+    p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
+    const int dkdv_tile = 32 * p->dkdv_wkv, dkdv_step = 32 * (4 / p->dkdv_wkv);
+    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd);
+    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->dq);
+    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, W, order, &p->dkdv);
+  }
+  append(p->image, p->fwd, &p->off_fwd_u, &p->off_fwd_o);
+  append(p->image, p->dkdv, &p->off_dkdv_u, &p->off_dkdv_o);
+  append(p->image, p->dq, &p->off_dq_u, &p->off_dq_o);
+  append(p->image, p->block, &p->off_blk_u, &p->off_blk_o);
+  p->plan_bytes = (int64_t)p->image.size() * 4;
+  p->di_off = align_up(p->plan_bytes, 256);
+  p->workspace_bytes = p->di_off + align_up(p->Tq * d.H * 4, 256);
+  *out = p;
+  return ok();
+}
+
+int jattn_plan_info(const jattn_plan* p, jattn_plan_summary* s) {
+  if (!p || !s) return fail(JATTN_E_NULL, "null argument to jattn_plan_info");
+  memset(s, 0, sizeof(*s));
+  s->workspace_bytes = p->workspace_bytes;
+  s->Tq = p->Tq;
+  s->Tk = p->Tk;
+  s->bias_elems = p->bias_elems;
+  s->flops_fwd = 4.0 * p->H * p->D * p->pairs;
+  s->flops_bwd = 2.5 * s->flops_fwd;
+  auto fill = [](const UnitList& L, jattn_kernel_plan* k) {
+    k->tile_rows = L.tile_rows;
+    k->step_rows = L.step_rows;
+    k->num_workers = L.num_workers;
+    k->n_units = (int32_t)L.n_units();
+  };
+  fill(p->fwd, &s->fwd);
+  fill(p->dkdv, &s->dkdv);
+  fill(p->dq, &s->dq);
+  fill(p->block, &s->block);
+  return ok();
+}
+
+int jattn_plan_export(const jattn_plan* p, int32_t which, int32_t* dst, int64_t cap, int64_t* n) {
+  if (!p || !n) return fail(JATTN_E_NULL, "null argument to jattn_plan_export");
+  const UnitList* L = nullptr;
+  switch (which / 2) {
+    case JATTN_PLAN_FWD: L = &p->fwd; break;
+    case JATTN_PLAN_DKDV: L = &p->dkdv; break;
+    case JATTN_PLAN_DQ: L = &p->dq; break;
+    case JATTN_PLAN_BLOCK: L = &p->block; break;
+    default: return fail(JATTN_E_ARG, "unknown plan part");
+  }
+  if (which < 0 || which > 7) return fail(JATTN_E_ARG, "unknown plan part");
+  const std::vector<int32_t>& v = (which % 2 == 0) ? L->units : L->offsets;
+  *n = (int64_t)v.size();
+  if (!dst) return ok();
+  if (cap < (int64_t)v.size()) return fail(JATTN_E_ARG, "export buffer too small");
+  if (!v.empty()) memcpy(dst, v.data(), v.size() * 4);
+  return ok();
+}
+
+int jattn_plan_upload(const jattn_plan* p, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (workspace_bytes < p->workspace_bytes) return fail(JATTN_E_WORKSPACE, "workspace too small");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (p->plan_bytes == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(workspace, p->image.data(), (size_t)p->plan_bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  // the source is pageable plan memory: wait so that the plan may be freed
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan)");
+  return ok();
+}
+
+int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias, void* o,
+              float* lse, void* workspace, void* stream) {
+  if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (p->Tq == 0) return ok();
+  if (!q || !o || (p->Tk > 0 && (!k || !v))) return fail(JATTN_E_NULL, "null q/k/v/o");
+  if (p->desc.has_bias && !bias && p->bias_elems > 0) return fail(JATTN_E_NULL, "bias required (has_bias = 1)");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(JATTN_E_ALIGN, "q/k/v/o must be 16-byte aligned");
+  const int es = elem_size(p->desc.in_dtype);
+  if (bias && !aligned(bias, (uintptr_t)es)) return fail(JATTN_E_ALIGN, "bias must be element-aligned");
+  if (lse && !aligned(lse, 4)) return fail(JATTN_E_ALIGN, "lse must be 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* samples = ws_ptr(workspace, p->off_samples);
+
+  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64) {
+    return fail(JATTN_E_UNSUPPORTED, "block-diagonal forward not built yet");
+  }
+  jattn::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bias = p->desc.has_bias ? bias : nullptr;
+  a.o = o;
+  a.lse = (p->desc.act == JATTN_SOFTMAX) ? lse : nullptr;
+  a.units = ws_ptr(workspace, p->off_fwd_u);
+  a.worker_off = ws_ptr(workspace, p->off_fwd_o);
+  a.samples = samples;
+  a.H = p->H;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.4426950408889634f;
+  KernelSel sel = base_sel(p);
+  sel.out_f32 = p->desc.out_dtype == JATTN_F32;
+  sel.wq = p->fwd_wq;
+  hipError_t e = jattn::launch_fwd(a, sel, p->fwd.num_workers, st);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
+int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias, const void* o,
+              const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* workspace,
+              void* stream) {
+  (void)q; (void)k; (void)v; (void)bias; (void)o; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
+  (void)dbias; (void)workspace; (void)stream;
+  if (!p) return fail(JATTN_E_NULL, "null plan");
+  return fail(JATTN_E_UNSUPPORTED, "backward not built yet");
+}
+
+void jattn_plan_destroy(jattn_plan* p) { delete p; }
+
+}  // extern "C"
+
+namespace jattn {
+
+hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.in_f32) {
+    if (k.D == 64) return launch_fwd_64_f32_f32(a, k, grid, st);
+    return launch_fwd_32_f32_f32(a, k, grid, st);
+  }
+  if (k.out_f32) {
+    if (k.D == 128) return launch_fwd_128_bf16_f32(a, k, grid, st);
+    if (k.D == 64) return launch_fwd_64_bf16_f32(a, k, grid, st);
+    return launch_fwd_32_bf16_f32(a, k, grid, st);
+  }
+  if (k.D == 128) return launch_fwd_128_bf16_bf16(a, k, grid, st);
+  if (k.D == 64) return launch_fwd_64_bf16_bf16(a, k, grid, st);
+  return launch_fwd_32_bf16_bf16(a, k, grid, st);
+}
+
+}  // namespace jattn

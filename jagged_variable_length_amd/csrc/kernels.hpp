@@ -1,0 +1,87 @@
+// Kernel argument blocks and launchers shared by the host library and the
+// device translation units.  Internal to libjattn.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jattn {
+
+// Plan pointers live in the caller's workspace (uploaded by jattn_plan_upload).
+struct PlanPtrs {
+  const int32_t* units;       // (b, h, tile, cost) per unit, in worker order
+  const int32_t* worker_off;  // [W + 1]
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  void* o;
+  float* lse;
+  const int32_t* units;
+  const int32_t* worker_off;
+  const int32_t* samples;  // 8 int32 per sample
+  int H;
+  float scale;       // softmax / activation scale
+  float scale_log2;  // scale * log2(e)
+};
+
+struct DiArgs {
+  const void* o;
+  const void* dout;
+  float* di;
+  int64_t rows;  // Tq * H
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  const void* dout;
+  const float* lse;  // [Tq, H] natural log
+  const float* di;   // [Tq, H]
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dbias;
+  const int32_t* units;
+  const int32_t* worker_off;
+  const int32_t* samples;
+  int H;
+  float scale;
+  float scale_log2;
+};
+
+// Which template instance to run.
+struct KernelSel {
+  int D;          // 32, 64, 128
+  int act;        // 0 softmax, 1 gelu, 2 silu
+  bool bias;      // additive bias input
+  bool dbias;     // write dBias
+  bool split;     // hi/lo bf16 operands for P / dS products
+  bool in_f32;    // inputs are fp32 (else bf16)
+  bool out_f32;   // O (fwd) or dQ/dK/dV (bwd) are fp32 (else bf16)
+  int wq;         // fwd/dq: waves along queries (4 or 1; 1 => 4-way key split)
+  int wkv;        // dkdv: waves along keys (4, 2 or 1; the rest split queries)
+};
+
+#define JATTN_FWD_LAUNCHER_(D, TI, TO) launch_fwd_##D##_##TI##_##TO
+#define JATTN_FWD_LAUNCHER(D, TI, TO) JATTN_FWD_LAUNCHER_(D, TI, TO)
+#define JATTN_DECLARE_FWD(D, TI, TO) \
+  hipError_t JATTN_FWD_LAUNCHER(D, TI, TO)(const FwdArgs&, const KernelSel&, int, hipStream_t);
+
+JATTN_DECLARE_FWD(128, bf16, bf16)
+JATTN_DECLARE_FWD(128, bf16, f32)
+JATTN_DECLARE_FWD(64, bf16, bf16)
+JATTN_DECLARE_FWD(64, bf16, f32)
+JATTN_DECLARE_FWD(64, f32, f32)
+JATTN_DECLARE_FWD(32, bf16, bf16)
+JATTN_DECLARE_FWD(32, bf16, f32)
+JATTN_DECLARE_FWD(32, f32, f32)
+
+hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+
+}  // namespace jattn

@@ -1,0 +1,40 @@
+// Host-side tile planner for jagged attention.
+//
+// "Training GEM at LLM scale" (Meta engineering post), section
+// "Generalized Dot-Product Attention (GDPA)", item "Software-level tile
+// scheduling for jagged tensors": the valid tiles of a jagged batch are listed
+// on the CPU before launch, empty tiles are never scheduled, and tiles are
+// assigned to compute units in zigzag order to even out the load.
+//
+// Units and their cost (inner-loop steps):
+//   fwd / dq : (b, h, q-tile)   for lq_b > 0, cost = ceil(lk_b / step_rows)
+//   dkdv     : (b, h, kv-tile)  for lk_b > 0, cost = ceil(lq_b / step_rows)
+//   block    : (b, h, 64-block) for l_b > 0,  cost = 1
+// Cost-0 units (partner length zero) only write zeros.  Units are stably
+// sorted by cost, descending, then dealt to workers round-robin
+// (heavy-first), boustrophedon (zigzag) or to the least-loaded worker (LPT).
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+namespace jattn {
+
+enum UnitKind { kKindFwd = 0, kKindDkdv = 1, kKindDq = 2, kKindBlock = 3 };
+enum Order { kHeavyFirst = 0, kZigzag = 1, kLpt = 2 };
+
+struct UnitList {
+  int32_t tile_rows = 0;
+  int32_t step_rows = 0;
+  int32_t num_workers = 0;
+  std::vector<int32_t> units;    // 4 int32 per unit: b, h, tile, cost
+  std::vector<int32_t> offsets;  // num_workers + 1
+  int64_t n_units() const { return (int64_t)units.size() / 4; }
+};
+
+// lq, lk: per-sample lengths (already validated).
+void plan_units(UnitKind kind, const std::vector<int32_t>& lq, const std::vector<int32_t>& lk, int H,
+                int tile_rows, int step_rows, int num_workers, Order order, UnitList* out);
+
+}  // namespace jattn

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+the fp64 oracle on the same seeded inputs, and compare element by element."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from jagged_variable_length_amd import attention as A
+from jagged_variable_length_amd import inputs as gen
+from oracle import attention as ora
+
+TOL = 2e-2  # max-abs bound on every output and gradient element
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_op(inp: gen.JaggedInputs, *, act="softmax", block=False, bias=False, want_dbias=False,
+            out_dtype=None, grad_dtype=None, split=False, order="heavy_first", num_workers=0):
+    op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, inp.H, inp.D, act=act, block_diagonal=block,
+                           has_bias=bias, want_dbias=want_dbias, in_dtype=inp.dtype, out_dtype=out_dtype,
+                           grad_dtype=grad_dtype, split_operands=split, order=order,
+                           num_workers=num_workers)
+    return op.upload()
+
+
+def device_inputs(inp: gen.JaggedInputs):
+    d = {n: A.to_device(getattr(inp, n), inp.dtype) for n in ("q", "k", "v")}
+    d["bias"] = A.to_device(inp.bias, inp.dtype) if inp.bias is not None else None
+    d["dout"] = A.to_device(inp.dout, inp.dtype) if inp.dout is not None else None
+    return d
+
+
+def oracle_fwd(inp, op):
+    return ora.forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_offsets, inp.kv_offsets,
+                       scale=op.scale, activation=op.act, block_diagonal=op.block_diagonal,
+                       bias=inp.f64("bias"))
+
+
+def oracle_bwd(inp, op):
+    return ora.backward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("dout"), inp.q_offsets,
+                        inp.kv_offsets, scale=op.scale, activation=op.act,
+                        block_diagonal=op.block_diagonal, bias=inp.f64("bias"),
+                        want_dbias=op.want_dbias)
+
+
+def max_err(got: np.ndarray, ref: np.ndarray, name: str):
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    return err, rms
+
+
+def check(got, ref, name, tol=TOL):
+    err, rms = max_err(got, ref, name)
+    say(f"  {name:6s} max|err| = {err:.3e}  (rms ref {rms:.3e}, tol {tol})")
+    assert err <= tol, f"{name}: max abs error {err} > {tol}"
+    return err
+
+
+def check_lse(got, ref, tol=TOL):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "LSE -inf pattern differs"
+    return check(got[fin], ref[fin], "lse", tol)
+
+
+def sync():
+    torch.cuda.synchronize()

@@ -1,0 +1,207 @@
+"""CPU-only checks of the C ABI: the library loads, exports what the header
+declares, validates its arguments on the host, and plans bit-exactly like the
+reference planner.  No GPU call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from jagged_variable_length_amd import binding as B
+from jagged_variable_length_amd import inputs as gen
+from oracle import plan as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libjattn.so not built (run python -m jagged_variable_length_amd.build)")
+    return B.lib()
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "jattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = _header_functions()
+    assert set(names) == set(B.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_covers_codes(lib):
+    for code in range(0, -10, -1):
+        assert B.jattn_strerror(code) != "unknown status"
+    assert B.jattn_strerror(-100) == "unknown status"
+
+
+def _desc(**kw):
+    d = B.jattn_desc()
+    d.B, d.H, d.D = kw.get("B", 2), kw.get("H", 2), kw.get("D", 64)
+    d.scale = kw.get("scale", 0.0)
+    d.act = kw.get("act", B.JATTN_SOFTMAX)
+    d.mask = kw.get("mask", B.JATTN_MASK_NONE)
+    d.has_bias = kw.get("has_bias", 0)
+    d.want_dbias = kw.get("want_dbias", 0)
+    d.in_dtype = kw.get("in_dtype", B.JATTN_BF16)
+    d.out_dtype = kw.get("out_dtype", B.JATTN_BF16)
+    d.grad_dtype = kw.get("grad_dtype", B.JATTN_BF16)
+    d.split_operands = kw.get("split", 0)
+    d.order = kw.get("order", B.JATTN_HEAVY_FIRST)
+    d.num_workers = kw.get("num_workers", 0)
+    return d
+
+
+@pytest.mark.parametrize("kw,qo,ko,code", [
+    (dict(), [1, 3, 5], [0, 2, 4], B.JATTN_E_OFFSETS),        # offsets[0] != 0
+    (dict(), [0, 3, 2], [0, 2, 4], B.JATTN_E_OFFSETS),        # decreasing
+    (dict(), [0, 3, 2 ** 31], [0, 2, 4], B.JATTN_E_OFFSETS),  # total >= 2^31
+    (dict(D=48), [0, 3, 5], [0, 2, 4], B.JATTN_E_SHAPE),
+    (dict(H=0), [0, 3, 5], [0, 2, 4], B.JATTN_E_SHAPE),
+    (dict(B=-1), [0], [0], B.JATTN_E_SHAPE),
+    (dict(mask=B.JATTN_MASK_BLOCKDIAG64), [0, 3, 5], [0, 2, 4], B.JATTN_E_SHAPE),  # lq != lk
+    (dict(act=7), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(in_dtype=B.JATTN_F32), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),  # f32 in, bf16 out
+    (dict(in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32, D=128),
+     [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(want_dbias=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(order=9), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(mask=B.JATTN_MASK_BLOCKDIAG64, act=B.JATTN_GELU_ERF), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+])
+def test_plan_create_rejects(lib, kw, qo, ko, code):
+    d = _desc(**kw)
+    with pytest.raises(B.JattnError) as e:
+        B.jattn_plan_create(d, qo, ko)
+    assert e.value.code == code
+    assert B.jattn_last_error() != ""
+
+
+def test_null_arguments(lib):
+    out = ctypes.c_void_p()
+    qo = np.array([0, 1], np.int64)
+    assert lib.jattn_plan_create(None, qo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 qo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(out)) == B.JATTN_E_NULL
+    d = _desc(B=1)
+    assert lib.jattn_plan_create(ctypes.byref(d), None, None, ctypes.byref(out)) == B.JATTN_E_NULL
+    assert lib.jattn_plan_info(None, None) == B.JATTN_E_NULL
+    assert lib.jattn_fwd(None, None, None, None, None, None, None, None, None) == B.JATTN_E_NULL
+    assert lib.jattn_bwd(*([None] * 14)) == B.JATTN_E_NULL
+
+
+def test_launch_validation_never_touches_gpu(lib):
+    """Bad pointers are rejected on the host before any HIP call."""
+    d = _desc(B=2, H=2, D=64)
+    p = B.jattn_plan_create(d, [0, 3, 5], [0, 2, 4])
+    try:
+        fake = 0x10000000  # never dereferenced: validation fails first
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_fwd(p, fake, fake, fake, None, fake, None, None, None)  # no workspace
+        assert e.value.code == B.JATTN_E_WORKSPACE
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_fwd(p, fake + 2, fake, fake, None, fake, None, fake, None)  # misaligned q
+        assert e.value.code == B.JATTN_E_ALIGN
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_fwd(p, None, fake, fake, None, fake, None, fake, None)
+        assert e.value.code == B.JATTN_E_NULL
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_plan_upload(p, fake, 16, None)  # too small
+        assert e.value.code == B.JATTN_E_WORKSPACE
+    finally:
+        B.jattn_plan_destroy(p)
+
+
+def test_bias_required_when_declared(lib):
+    d = _desc(B=2, H=2, D=64, has_bias=1)
+    p = B.jattn_plan_create(d, [0, 3, 5], [0, 2, 4])
+    try:
+        fake = 0x10000000
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_fwd(p, fake, fake, fake, None, fake, None, fake, None)
+        assert e.value.code == B.JATTN_E_NULL
+    finally:
+        B.jattn_plan_destroy(p)
+
+
+# ---------------------------------------------------------------------------
+# plans: bit-exact against the reference planner
+# ---------------------------------------------------------------------------
+def _compare_plan(p, lq, lk, H, block):
+    info = B.jattn_plan_info(p)
+    parts = [("block", B.JATTN_PLAN_BLOCK, info.block)] if block else [
+        ("fwd", B.JATTN_PLAN_FWD, info.fwd), ("dkdv", B.JATTN_PLAN_DKDV, info.dkdv),
+        ("dq", B.JATTN_PLAN_DQ, info.dq)]
+    return info, parts
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("order", ["heavy_first", "zigzag", "lpt"])
+def test_plans_match_reference_planner(lib, cfg, order):
+    w = gen.WORKLOADS[cfg]
+    lq, lk = gen.make_lengths(cfg, cfg)
+    qo, ko = gen.offsets_from_lengths(lq), gen.offsets_from_lengths(lk)
+    d = _desc(B=w.B, H=w.H, D=w.D, act={"softmax": 0, "gelu": 1, "silu": 2}[w.act],
+              mask=1 if w.block_diagonal else 0, has_bias=int(w.bias), want_dbias=int(w.want_dbias),
+              in_dtype=B.JATTN_F32 if w.dtype == "f32" else B.JATTN_BF16,
+              out_dtype=B.JATTN_F32 if w.out_dtype == "f32" else B.JATTN_BF16,
+              grad_dtype=B.JATTN_F32 if w.grad_dtype == "f32" else B.JATTN_BF16,
+              order={"heavy_first": 0, "zigzag": 1, "lpt": 2}[order], num_workers=0 if cfg else 7)
+    p = B.jattn_plan_create(d, qo, ko)
+    try:
+        info, parts = _compare_plan(p, lq, lk, w.H, w.block_diagonal)
+        assert info.Tq == qo[-1] and info.Tk == ko[-1]
+        for kind, which, kp in parts:
+            units = B.jattn_plan_export(p, which * 2 + 0).reshape(-1, 4)
+            offs = B.jattn_plan_export(p, which * 2 + 1)
+            ref_units, ref_offs = P.plan(kind, lq.tolist(), lk.tolist(), w.H, kp.tile_rows, kp.step_rows,
+                                         kp.num_workers, order)
+            assert kp.n_units == len(ref_units)
+            np.testing.assert_array_equal(units, np.array(ref_units, dtype=np.int32).reshape(-1, 4))
+            np.testing.assert_array_equal(offs, np.array(ref_offs, dtype=np.int32))
+        pairs = sum(min(64, l - s) ** 2 for l in lq for s in range(0, l, 64)) if w.block_diagonal \
+            else int(np.sum(lq * lk))
+        assert info.flops_fwd == pytest.approx(4.0 * w.H * w.D * pairs, rel=1e-12)
+    finally:
+        B.jattn_plan_destroy(p)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_plans_match(lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    Bn = int(rng.integers(1, 40))
+    lq = rng.integers(0, 400, Bn)
+    lk = rng.integers(0, 300, Bn) if seed % 2 else lq.copy()
+    qo, ko = gen.offsets_from_lengths(lq), gen.offsets_from_lengths(lk)
+    W = int(rng.integers(1, 50))
+    block = seed % 2 == 0 and seed % 4 == 0
+    for order in range(3):
+        d = _desc(B=Bn, H=3, D=64, order=order, num_workers=W, mask=1 if block else 0)
+        p = B.jattn_plan_create(d, qo, ko)
+        try:
+            info, parts = _compare_plan(p, lq, lk, 3, block)
+            for kind, which, kp in parts:
+                units = B.jattn_plan_export(p, which * 2).reshape(-1, 4)
+                offs = B.jattn_plan_export(p, which * 2 + 1)
+                ref_u, ref_o = P.plan(kind, lq.tolist(), lk.tolist(), 3, kp.tile_rows, kp.step_rows, W,
+                                      ["heavy_first", "zigzag", "lpt"][order])
+                np.testing.assert_array_equal(units, np.array(ref_u, np.int32).reshape(-1, 4))
+                np.testing.assert_array_equal(offs, np.array(ref_o, np.int32))
+        finally:
+            B.jattn_plan_destroy(p)
+
+
+def test_empty_batch_plans(lib):
+    d = _desc(B=0)
+    p = B.jattn_plan_create(d, [0], [0])
+    try:
+        info = B.jattn_plan_info(p)
+        assert info.Tq == 0 and info.fwd.n_units == 0
+        # a forward over nothing is a no-op that touches no pointer
+        B.jattn_fwd(p, None, None, None, None, None, None, None, None)
+    finally:
+        B.jattn_plan_destroy(p)

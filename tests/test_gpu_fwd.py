@@ -1,0 +1,119 @@
+"""GPU parity of the forward kernels against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from jagged_variable_length_amd import attention as A
+from jagged_variable_length_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check, check_lse, device_inputs, make_op, oracle_fwd, say, sync  # noqa: E402
+from oracle import attention as ora  # noqa: E402
+
+
+def _run_fwd(inp, **kw):
+    op = make_op(inp, **kw)
+    d = device_inputs(inp)
+    o, lse = op.forward(d["q"], d["k"], d["v"], bias=d["bias"])
+    sync()
+    return op, A.to_f64(o), (A.to_f64(lse) if lse is not None else None)
+
+
+def _compare(inp, op, o, lse):
+    ro, rl = oracle_fwd(inp, op)
+    check(o, ro, "O")
+    if rl is not None and lse is not None:
+        check_lse(lse, rl)
+
+
+def test_fwd_config0_f32():
+    say("case: config 0 (fp32, D=32, zero-length sample)")
+    inp = gen.make_inputs(0, 0)
+    op, o, lse = _run_fwd(inp, out_dtype="f32", grad_dtype="f32")
+    _compare(inp, op, o, lse)
+
+
+@pytest.mark.parametrize("D", [128, 64, 32])
+@pytest.mark.parametrize("bias", [False, True])
+def test_fwd_softmax_ragged(D, bias):
+    say(f"case: softmax ragged D={D} bias={bias}")
+    lq = [1, 0, 130, 64, 257, 33, 7, 500]
+    lk = [5, 9, 0, 64, 300, 1, 129, 70]
+    inp = gen.make_custom(lq, lk, 3, D, "bf16", seed=D + bias, bias=bias)
+    op, o, lse = _run_fwd(inp, bias=bias)
+    _compare(inp, op, o, lse)
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("split", [False, True])
+def test_fwd_gdpa(act, split):
+    say(f"case: gdpa {act} split={split}")
+    lq = [32, 32, 0, 32, 32]
+    lk = [64, 300, 50, 0, 1000]
+    inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=5)
+    op, o, _ = _run_fwd(inp, act=act, split=split, out_dtype="f32")
+    assert op.info.fwd.tile_rows == 32  # short-query shape: key tiles split over waves
+    if split:
+        _compare(inp, op, o, None)
+        return
+    # Without the hi/lo split, P enters the PV product rounded to bf16: the
+    # error is bounded by u * (|P| |V|) with u = 2^-8 (bf16 unit roundoff).
+    ro, _ = oracle_fwd(inp, op)
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    act_fn = {"gelu": ora.gelu, "silu": ora.silu}[act]
+    for b in range(inp.B):
+        sq = slice(inp.q_offsets[b], inp.q_offsets[b + 1])
+        sk = slice(inp.kv_offsets[b], inp.kv_offsets[b + 1])
+        for h in range(inp.H):
+            P = act_fn(op.scale * q[sq, h] @ k[sk, h].T)
+            bound = 2.0 ** -8 * (np.abs(P) @ np.abs(v[sk, h])) + 1e-3
+            assert np.all(np.abs(o[sq, h] - ro[sq, h]) <= bound), (b, h)
+
+
+def test_fwd_short_query_softmax_split_keys():
+    say("case: softmax with 32-row queries (key-split combine)")
+    lq = [32, 20, 1, 32]
+    lk = [700, 0, 129, 64]
+    inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=6, bias=True)
+    op, o, lse = _run_fwd(inp, bias=True)
+    assert op.info.fwd.tile_rows == 32
+    _compare(inp, op, o, lse)
+
+
+def test_fwd_outputs_overwrite_garbage():
+    """Zero-length samples are written by the library, not assumed zero."""
+    say("case: garbage-filled outputs")
+    lq, lk = [3, 10, 0], [0, 4, 5]
+    inp = gen.make_custom(lq, lk, 2, 64, "bf16", seed=8)
+    op = make_op(inp)
+    d = device_inputs(inp)
+    o = torch.full((op.Tq, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((op.Tq, 2), 7.0, dtype=torch.float32, device="cuda")
+    op.forward(d["q"], d["k"], d["v"], o=o, lse=lse)
+    sync()
+    _compare(inp, op, A.to_f64(o), A.to_f64(lse))
+
+
+def test_fwd_deterministic():
+    say("case: run-to-run bitwise identical")
+    inp = gen.make_custom([300, 17, 900], [250, 1000, 3], 4, 128, "bf16", seed=9, bias=True)
+    op = make_op(inp, bias=True)
+    d = device_inputs(inp)
+    o1, l1 = op.forward(d["q"], d["k"], d["v"], bias=d["bias"])
+    o2, l2 = op.forward(d["q"], d["k"], d["v"], bias=d["bias"])
+    sync()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("order", ["zigzag", "lpt"])
+def test_fwd_orders_agree(order):
+    say(f"case: order {order}")
+    inp = gen.make_custom([300, 17, 900, 45], [250, 1000, 3, 64], 2, 64, "bf16", seed=10)
+    op1 = make_op(inp)
+    op2 = make_op(inp, order=order, num_workers=13)
+    d = device_inputs(inp)
+    o1, l1 = op1.forward(d["q"], d["k"], d["v"])
+    o2, l2 = op2.forward(d["q"], d["k"], d["v"])
+    sync()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
