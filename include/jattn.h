@@ -26,7 +26,7 @@
  *   bias, dbias        samples concatenated: sample b is [H, lq_b, lk_b]
  *                      row-major at element offset sum_{j<b} H lq_j lk_j
  *   offsets            host int64 [B+1], offsets[0] = 0, non-decreasing.
- * Value pointers must be 16-byte aligned; bias/dbias 4-byte aligned.
+ * Value pointers must be 16-byte aligned; bias/dbias element-aligned.
  *
  * Ownership and threading.  The caller owns every device buffer, including
  * the workspace (size from jattn_plan_info).  The library never allocates
@@ -97,7 +97,7 @@ typedef struct {
   int32_t want_dbias;   /* 0/1: backward writes dBias (needs has_bias) */
   int32_t in_dtype;     /* q, k, v, bias, dout: JATTN_BF16 | JATTN_F32 */
   int32_t out_dtype;    /* o */
-  int32_t grad_dtype;   /* dq, dk, dv (dbias always uses in_dtype) */
+  int32_t grad_dtype;   /* dq, dk, dv, dbias */
   int32_t split_operands; /* 0/1: P and dS enter the PV-type products as
                              bf16 hi + lo pairs (two MFMAs) for accuracy */
   int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
@@ -154,7 +154,7 @@ int jattn_fwd(const jattn_plan* plan, const void* q, const void* k, const void* 
               const void* bias, void* o, float* lse, void* workspace, void* stream);
 
 /* Backward.  Given dout, writes dq, dk, dv (grad_dtype) and, if
- * desc.want_dbias, dbias (in_dtype).  Softmax with mask NONE needs o and
+ * desc.want_dbias, dbias (grad_dtype).  Softmax with mask NONE needs o and
  * the forward's lse (JATTN_E_STATE otherwise); GDPA needs neither; block
  * mode recomputes its row statistics in-tile and needs neither.  Uses the
  * workspace's scratch region for row statistics.  No atomics: every output

@@ -92,7 +92,7 @@ class JaggedAttention:
         dk = dk if dk is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         if self.want_dbias and dbias is None:
-            dbias = torch.empty(int(self.info.bias_elems), dtype=_TORCH_DT[self.in_dtype], device=self.device)
+            dbias = torch.empty(int(self.info.bias_elems), dtype=gdt, device=self.device)
         _b.jattn_bwd(self.plan, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout),
                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
         return dq, dk, dv, dbias

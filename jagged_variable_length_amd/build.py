@@ -35,6 +35,8 @@ def units():
     u = [("api.cpp", "api", []), ("planner.cpp", "planner", [])]
     for d, ti, to in FWD_INST:
         u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
+        di = ["-DJ_DI"] if ti == to else []  # Di launcher once per (D, dO type)
+        u.append(("bwd_inst.hip", f"bwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TG={to}"] + di))
     return u
 
 

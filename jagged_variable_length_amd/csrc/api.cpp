@@ -313,10 +313,67 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
 int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias, const void* o,
               const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* workspace,
               void* stream) {
-  (void)q; (void)k; (void)v; (void)bias; (void)o; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
-  (void)dbias; (void)workspace; (void)stream;
   if (!p) return fail(JATTN_E_NULL, "null plan");
-  return fail(JATTN_E_UNSUPPORTED, "backward not built yet");
+  if (p->Tq == 0 && p->Tk == 0) return ok();
+  const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask == JATTN_MASK_NONE;
+  if ((p->Tq > 0 && (!q || !dout || !dq)) || (p->Tk > 0 && (!k || !v || !dk || !dv)))
+    return fail(JATTN_E_NULL, "null q/k/v/dout/dq/dk/dv");
+  if (p->desc.has_bias && !bias && p->bias_elems > 0) return fail(JATTN_E_NULL, "bias required (has_bias = 1)");
+  if (p->desc.want_dbias && !dbias && p->bias_elems > 0) return fail(JATTN_E_NULL, "dbias required (want_dbias = 1)");
+  if (softmax_dense && p->Tq > 0 && (!o || !lse)) return fail(JATTN_E_STATE, "softmax backward needs o and lse");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16) || !aligned(o, 16))
+    return fail(JATTN_E_ALIGN, "value tensors must be 16-byte aligned");
+  const int es = elem_size(p->desc.in_dtype);
+  if ((bias && !aligned(bias, (uintptr_t)es)) || (dbias && !aligned(dbias, (uintptr_t)elem_size(p->desc.grad_dtype))))
+    return fail(JATTN_E_ALIGN, "bias/dbias must be element-aligned");
+  if (lse && !aligned(lse, 4)) return fail(JATTN_E_ALIGN, "lse must be 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64)
+    return fail(JATTN_E_UNSUPPORTED, "block-diagonal backward not built yet");
+
+  float* di = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->di_off);
+  KernelSel sel = base_sel(p);
+  sel.out_f32 = p->desc.grad_dtype == JATTN_F32;
+  sel.wq = p->dq_wq;
+  sel.wkv = p->dkdv_wkv;
+  hipError_t e;
+  if (softmax_dense && p->Tq > 0) {
+    jattn::DiArgs da{o, dout, di, p->Tq * p->H};
+    e = jattn::launch_di(da, sel, p->desc.out_dtype == JATTN_F32, st);
+    if (e != hipSuccess) return hip_fail(e, "Di launch");
+  }
+  jattn::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bias = p->desc.has_bias ? bias : nullptr;
+  a.dout = dout;
+  a.lse = lse;
+  a.di = di;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dbias = p->desc.want_dbias ? dbias : nullptr;
+  a.samples = ws_ptr(workspace, p->off_samples);
+  a.H = p->H;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.4426950408889634f;
+  if (p->dkdv.n_units() > 0) {
+    a.units = ws_ptr(workspace, p->off_dkdv_u);
+    a.worker_off = ws_ptr(workspace, p->off_dkdv_o);
+    e = jattn::launch_dkdv(a, sel, p->dkdv.num_workers, st);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  }
+  if (p->dq.n_units() > 0) {
+    a.units = ws_ptr(workspace, p->off_dq_u);
+    a.worker_off = ws_ptr(workspace, p->off_dq_o);
+    e = jattn::launch_dq(a, sel, p->dq.num_workers, st);
+    if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  }
+  return ok();
 }
 
 void jattn_plan_destroy(jattn_plan* p) { delete p; }
@@ -338,6 +395,35 @@ hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_
   if (k.D == 128) return launch_fwd_128_bf16_bf16(a, k, grid, st);
   if (k.D == 64) return launch_fwd_64_bf16_bf16(a, k, grid, st);
   return launch_fwd_32_bf16_bf16(a, k, grid, st);
+}
+
+#define JATTN_DISPATCH_BWD(KIND)                                              \
+  hipError_t launch_##KIND(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) { \
+    if (k.in_f32) {                                                              \
+      if (k.D == 64) return launch_##KIND##_64_f32_f32(a, k, grid, st);          \
+      return launch_##KIND##_32_f32_f32(a, k, grid, st);                         \
+    }                                                                            \
+    if (k.out_f32) {                                                             \
+      if (k.D == 128) return launch_##KIND##_128_bf16_f32(a, k, grid, st);       \
+      if (k.D == 64) return launch_##KIND##_64_bf16_f32(a, k, grid, st);         \
+      return launch_##KIND##_32_bf16_f32(a, k, grid, st);                        \
+    }                                                                            \
+    if (k.D == 128) return launch_##KIND##_128_bf16_bf16(a, k, grid, st);        \
+    if (k.D == 64) return launch_##KIND##_64_bf16_bf16(a, k, grid, st);          \
+    return launch_##KIND##_32_bf16_bf16(a, k, grid, st);                         \
+  }
+
+JATTN_DISPATCH_BWD(dq)
+JATTN_DISPATCH_BWD(dkdv)
+
+hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_t st) {
+  if (k.in_f32) {
+    if (k.D == 64) return launch_di_64_f32(a, o_f32, st);
+    return launch_di_32_f32(a, o_f32, st);
+  }
+  if (k.D == 128) return launch_di_128_bf16(a, o_f32, st);
+  if (k.D == 64) return launch_di_64_bf16(a, o_f32, st);
+  return launch_di_32_bf16(a, o_f32, st);
 }
 
 }  // namespace jattn

@@ -44,6 +44,16 @@ struct FwdShape {
   static_assert(kThreads % BN == 0, "bias staging assumes BN | 256");
 };
 
+// Value of a probability as the PV MFMA consumes it (bf16 operands are
+// rounded to nearest even; fp32 operands are exact).
+template <typename TI>
+__device__ __forceinline__ float round_p(float x) {
+  if constexpr (sizeof(TI) == 2)
+    return (float)(bf16)x;
+  else
+    return x;
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
 template <>
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int SZ = (int)sizeof(TI);
 
   constexpr int kStageBytes = SZ * (BN * KPITCH + D * VPITCH + (BIAS ? BM * BPITCH : 0));
-  constexpr int kCombineBytes = (WK > 1) ? (int)sizeof(float) * (WK * D * 32 + 2 * WK * 32) : 0;
+  constexpr int kCombineBytes = (WK > 1) ? (int)sizeof(float) * (WK * D * 32 + 3 * WK * 32) : 0;
   constexpr int kSmem = kStageBytes > kCombineBytes ? kStageBytes : kCombineBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   TI* Ks = reinterpret_cast<TI*>(smem);
@@ -160,7 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < ND; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY;  // running max (log2 units), softmax only
-    float l_run = 0.0f;       // this lane's partial row sum
+    float l_run = 0.0f;       // this lane's partial row sum (exact P, for LSE)
+    float lr_run = 0.0f;      // same with P as the PV product sees it (for O)
 
     // register prefetch of one tile
     i32x4 kreg[CPT], vreg[CPT];
@@ -254,17 +265,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         mx = wave_xor32_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2f(m_run - m_new);
-        float rs = 0.0f;
+        float rs = 0.0f, rsr = 0.0f;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
+            // O is normalised by the sum of P exactly as the PV product sees
+            // it, so that it stays a convex combination of V rows; LSE keeps
+            // the exact sum
             const float e = exp2f(p[nb][i] - m_new);
-            p[nb][i] = e;
+            const float er = round_p<TI>(e);
+            p[nb][i] = er;
             rs += e;
+            rsr += er;
           }
         }
         l_run = l_run * alpha + rs;
+        lr_run = lr_run * alpha + rsr;
         m_run = m_new;
 #pragma unroll
         for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
@@ -331,12 +348,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
           npad += 32 - valid;
         }
       }
-      float l_tot = wave_xor32_sum(l_run);
-      l_tot -= (float)npad * exp2f(-m_run);
-      l_run = l_tot;
+      const float pad_e = exp2f(-m_run);
+      l_run = wave_xor32_sum(l_run) - (float)npad * pad_e;
+      lr_run = wave_xor32_sum(lr_run) - (float)npad * round_p<TI>(pad_e);
       if constexpr (WK == 1) {
-        scale_out = (s.lk > 0) ? 1.0f / l_tot : 0.0f;
-        lse2 = (s.lk > 0) ? m_run + __log2f(l_tot) : -INFINITY;
+        scale_out = (s.lk > 0) ? 1.0f / lr_run : 0.0f;
+        lse2 = (s.lk > 0) ? m_run + __log2f(l_run) : -INFINITY;
       }
     }
 
@@ -362,6 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       float* part = reinterpret_cast<float*>(smem);  // [WK][D][32] partial O
       float* mpart = part + WK * D * 32;             // [WK][32]
       float* lpart = mpart + WK * 32;                // [WK][32]
+      float* lrpart = lpart + WK * 32;               // [WK][32]
       __syncthreads();  // all waves done with the last tile
 #pragma unroll
       for (int d = 0; d < ND; ++d)
@@ -370,10 +388,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       if (g == 0) {
         mpart[wk * 32 + l32] = m_run;
         lpart[wk * 32 + l32] = l_run;
+        lrpart[wk * 32 + l32] = lr_run;
       }
       __syncthreads();
       // wave w finishes head-dim columns [w*D/4, (w+1)*D/4) for all 32 rows
-      float mall = -INFINITY, lall = 0.0f;
+      float mall = -INFINITY, lall = 0.0f, lrall = 0.0f;
       float fw[WK];
       if constexpr (SOFTMAX) {
 #pragma unroll
@@ -383,12 +402,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
           // a sample without keys has every partial at m = -inf: weight 0
           fw[w2] = (s.lk > 0) ? exp2f(mpart[w2 * 32 + l32] - mall) : 0.0f;
           lall += lpart[w2 * 32 + l32] * fw[w2];
+          lrall += lrpart[w2 * 32 + l32] * fw[w2];
         }
       } else {
 #pragma unroll
         for (int w2 = 0; w2 < WK; ++w2) fw[w2] = 1.0f;
       }
-      const float inv = SOFTMAX ? ((s.lk > 0) ? 1.0f / lall : 0.0f) : 1.0f;
+      const float inv = SOFTMAX ? ((s.lk > 0) ? 1.0f / lrall : 0.0f) : 1.0f;
       constexpr int DC = D / WK;  // columns per wave
       const int row = qt * BM + l32;
       if (row < s.lq) {

@@ -82,6 +82,33 @@ JATTN_DECLARE_FWD(32, bf16, bf16)
 JATTN_DECLARE_FWD(32, bf16, f32)
 JATTN_DECLARE_FWD(32, f32, f32)
 
+#define JATTN_BWD_LAUNCHER_(K, D, TI, TG) launch_##K##_##D##_##TI##_##TG
+#define JATTN_BWD_LAUNCHER(K, D, TI, TG) JATTN_BWD_LAUNCHER_(K, D, TI, TG)
+#define JATTN_DECLARE_BWD(D, TI, TG)                                                                  \
+  hipError_t JATTN_BWD_LAUNCHER(dq, D, TI, TG)(const BwdArgs&, const KernelSel&, int, hipStream_t);   \
+  hipError_t JATTN_BWD_LAUNCHER(dkdv, D, TI, TG)(const BwdArgs&, const KernelSel&, int, hipStream_t);
+
+JATTN_DECLARE_BWD(128, bf16, bf16)
+JATTN_DECLARE_BWD(128, bf16, f32)
+JATTN_DECLARE_BWD(64, bf16, bf16)
+JATTN_DECLARE_BWD(64, bf16, f32)
+JATTN_DECLARE_BWD(64, f32, f32)
+JATTN_DECLARE_BWD(32, bf16, bf16)
+JATTN_DECLARE_BWD(32, bf16, f32)
+JATTN_DECLARE_BWD(32, f32, f32)
+
+#define JATTN_DI_LAUNCHER_(D, TI) launch_di_##D##_##TI
+#define JATTN_DI_LAUNCHER(D, TI) JATTN_DI_LAUNCHER_(D, TI)
+#define JATTN_DECLARE_DI(D, TI) hipError_t JATTN_DI_LAUNCHER(D, TI)(const DiArgs&, bool, hipStream_t);
+JATTN_DECLARE_DI(128, bf16)
+JATTN_DECLARE_DI(64, bf16)
+JATTN_DECLARE_DI(64, f32)
+JATTN_DECLARE_DI(32, bf16)
+JATTN_DECLARE_DI(32, f32)
+
 hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+hipError_t launch_dq(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_t st);
 
 }  // namespace jattn
