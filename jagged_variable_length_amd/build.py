@@ -32,7 +32,7 @@ FWD_INST = [(128, "bf16", "bf16"), (128, "bf16", "f32"), (64, "bf16", "bf16"), (
 
 
 def units():
-    u = [("api.cpp", "api", []), ("planner.cpp", "planner", [])]
+    u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", [])]
     for d, ti, to in FWD_INST:
         u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
         di = ["-DJ_DI"] if ti == to else []  # Di launcher once per (D, dO type)

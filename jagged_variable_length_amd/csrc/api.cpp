@@ -123,6 +123,10 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   if (d.has_bias != 0 && d.has_bias != 1) return fail(JATTN_E_ARG, "has_bias must be 0 or 1");
   if (d.mask == JATTN_MASK_BLOCKDIAG64 && (d.act != JATTN_SOFTMAX || d.has_bias))
     return fail(JATTN_E_UNSUPPORTED, "block-diagonal mode supports softmax without bias");
+  if (d.mask == JATTN_MASK_BLOCKDIAG64 && d.in_dtype != JATTN_BF16)
+    return fail(JATTN_E_UNSUPPORTED, "block-diagonal mode needs bf16 inputs");
+  if (d.mask == JATTN_MASK_BLOCKDIAG64 && (d.num_workers % 2) != 0)
+    return fail(JATTN_E_ARG, "block-diagonal mode needs an even num_workers (two per workgroup)");
   if (d.order < JATTN_HEAVY_FIRST || d.order > JATTN_LPT) return fail(JATTN_E_ARG, "unknown order");
   if (d.num_workers < 0 || d.num_workers > 65536) return fail(JATTN_E_ARG, "num_workers out of range");
   if (!(d.scale == d.scale) || isinf(d.scale)) return fail(JATTN_E_ARG, "scale must be finite");
@@ -186,7 +190,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   p->bias_elems = bias0;
   p->off_samples = 0;
 
-  const int W = d.num_workers > 0 ? d.num_workers : kDefaultWorkers;
+  const int W = d.num_workers > 0 ? d.num_workers
+                                  : (d.mask == JATTN_MASK_BLOCKDIAG64 ? 2 * kDefaultWorkers : kDefaultWorkers);
   const jattn::Order order = (jattn::Order)d.order;
   if (d.mask == JATTN_MASK_BLOCKDIAG64) {
     jattn::plan_units(jattn::kKindBlock, lq, lk, d.H, 64, 64, W, order, &p->block);
@@ -286,9 +291,6 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* samples = ws_ptr(workspace, p->off_samples);
 
-  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64) {
-    return fail(JATTN_E_UNSUPPORTED, "block-diagonal forward not built yet");
-  }
   jattn::FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -305,7 +307,16 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   KernelSel sel = base_sel(p);
   sel.out_f32 = p->desc.out_dtype == JATTN_F32;
   sel.wq = p->fwd_wq;
-  hipError_t e = jattn::launch_fwd(a, sel, p->fwd.num_workers, st);
+  hipError_t e;
+  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64) {
+    if (p->block.n_units() == 0) return ok();
+    a.lse = nullptr;  // no row statistics leave a block
+    a.units = ws_ptr(workspace, p->off_blk_u);
+    a.worker_off = ws_ptr(workspace, p->off_blk_o);
+    e = jattn::launch_block_fwd(a, sel, p->block.num_workers / 2, st);
+  } else {
+    e = jattn::launch_fwd(a, sel, p->fwd.num_workers, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return ok();
 }
@@ -331,8 +342,6 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
     return fail(JATTN_E_ALIGN, "bias/dbias must be element-aligned");
   if (lse && !aligned(lse, 4)) return fail(JATTN_E_ALIGN, "lse must be 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64)
-    return fail(JATTN_E_UNSUPPORTED, "block-diagonal backward not built yet");
 
   float* di = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->di_off);
   KernelSel sel = base_sel(p);
@@ -340,6 +349,26 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   sel.wq = p->dq_wq;
   sel.wkv = p->dkdv_wkv;
   hipError_t e;
+  if (p->desc.mask == JATTN_MASK_BLOCKDIAG64) {
+    if (p->block.n_units() == 0) return ok();
+    jattn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.units = ws_ptr(workspace, p->off_blk_u);
+    a.worker_off = ws_ptr(workspace, p->off_blk_o);
+    a.samples = ws_ptr(workspace, p->off_samples);
+    a.H = p->H;
+    a.scale = p->scale;
+    a.scale_log2 = p->scale * 1.4426950408889634f;
+    e = jattn::launch_block_bwd(a, sel, p->block.num_workers / 2, st);
+    if (e != hipSuccess) return hip_fail(e, "block backward launch");
+    return ok();
+  }
   if (softmax_dense && p->Tq > 0) {
     jattn::DiArgs da{o, dout, di, p->Tq * p->H};
     e = jattn::launch_di(da, sel, p->desc.out_dtype == JATTN_F32, st);

@@ -1,0 +1,397 @@
+// BlockAttention kernels (fixed 64-token block-diagonal mask), gfx950.
+//
+// Method: "Training GEM at LLM scale" (Meta engineering post), section
+// "BlockAttention": each 64-token query block attends only to the key/value
+// block with the same index, so attention splits into independent 64 x 64
+// problems.  A dedicated kernel then needs no online-softmax correction, no
+// logsumexp written to memory and no separate Di pass.
+//
+// Forward : one wave per block.  K and V of the block go straight from HBM
+//           into the wave's LDS (buffer loads with LDS destination; rows past
+//           the sample end come back as zero), Q goes to registers.  The full
+//           64-key softmax row lives in one lane, so one pass computes m, l
+//           and P; the zero rows of a partial last block are removed by
+//           subtracting their exp(0 - m) terms.
+// Backward: two waves per block (two blocks per workgroup).  Phase 1, lane =
+//           query row: S^T, softmax, dP^T, Di = sum_j P dP (in-tile), dS,
+//           dQ = dS K.  Phase 2, lane = key row: S, dP again, P from the
+//           phase-1 row statistics, dV = P^T dO, dK = dS^T Q.
+// Operands that are contracted along rows (V^T, K^T, Q^T, dO^T) are read
+// from the row-major LDS tiles with ds_read_b64_tr_b16.
+#pragma once
+#include "common.hpp"
+#include "fwd_impl.hpp"
+#include "kernels.hpp"
+
+namespace jattn {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// Row-major bf16 tile in LDS with 16-byte chunks XOR-swizzled per row.
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RB = D * 2;         // bytes per row
+  static constexpr int BYTES = 64 * RB;    // 64 rows
+  static __device__ __forceinline__ int swz(int r) { return r & (CPR - 1); }
+  // byte offset of element (r, col) (col multiple of 4)
+  static __device__ __forceinline__ int off(int r, int col) {
+    const int c = col >> 3;
+    return r * RB + ((c ^ swz(r)) << 4) + ((col & 4) << 1);
+  }
+};
+
+// Issue the loads of one 64-row tile (rows row0.. of a sample/head) straight
+// into LDS.  `part`/`nparts` split the CPR instructions among waves.
+template <int D>
+__device__ __forceinline__ void load_tile_async(char* lds_tile, rsrc_t r, int row0, int HD, int lane, int part,
+                                                int nparts) {
+  using T = Tile<D>;
+  constexpr int RPI = 64 / T::CPR;  // rows per instruction (64 lanes x 16 B)
+  for (int inst = part; inst < T::CPR; inst += nparts) {
+    const int rr = inst * RPI + lane / T::CPR;  // tile row this lane fills
+    const int p = lane % T::CPR;                // LDS chunk position in that row
+    const int c = p ^ T::swz(rr);               // logical chunk that belongs there
+    const uint32_t voff = (uint32_t)((row0 + rr) * HD + c * 8) * 2;
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_tile + inst * 1024), 16,
+                                             voff, 0, 0, 0);
+#endif
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  // s_waitcnt vmcnt(0): buffer loads into LDS have landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// bf16 fragment from 8 consecutive accumulator slots
+__device__ __forceinline__ bf16x8 pack8_from(const f32x16& v, int off) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)v[off + j];
+  return r;
+}
+
+// A/B fragment of a row operand: lane (row = base + l%32, k chunk kk*2 + g).
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int kk, int g) {
+  return *reinterpret_cast<const bf16x8*>(tile + Tile<D>::off(row, kk * 16 + g * 8));
+}
+
+// A fragment of a transposed operand X^T (32 columns of X x 16 rows of X):
+// lane l gets X[rows][col0 + l%32] for the 8 rows that the accumulator slot
+// order of block `blk`, step `st` assigns to lane half g.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int blk, int st, int col0, int lane) {
+  const int i = lane & 15, grp = (lane >> 4) & 1, g = lane >> 5;
+  const int col = col0 + 16 * grp + 4 * (i & 3);
+  const int r1 = blk * 32 + 16 * st + 4 * g + (i >> 2);
+  v4i16 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if __HIP_DEVICE_COMPILE__
+  lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + Tile<D>::off(r1, col)));
+  hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + Tile<D>::off(r1 + 8, col)));
+#endif
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// forward: one wave = one 64 x 64 block
+// ---------------------------------------------------------------------------
+template <typename TO, int D>
+__global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
+  using T = Tile<D>;
+  constexpr int NKK = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * T::BYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  char* kt = smem + wave * 2 * T::BYTES;
+  char* vt = kt + T::BYTES;
+  // two waves share one worker (wave pair) and take alternate units of it
+  const int worker = xcd_worker(blockIdx.x, gridDim.x) * 2 + (wave >> 1);
+  const int u_end = a.worker_off[worker + 1];
+  const int HD = a.H * D;
+
+  for (int u = a.worker_off[worker] + (wave & 1); u < u_end; u += 2) {
+    const i32x4 unit = reinterpret_cast<const i32x4*>(a.units)[u];
+    const int b = unit[0], h = unit[1], t = unit[2];
+    const Sample s = load_sample(a.samples, b);
+    const int row0 = t * 64;
+    const int r = min(64, s.lq - row0);  // valid rows of this block
+    const int64_t base = ((int64_t)(s.k0 + row0) * a.H + h) * D;
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + base, (uint32_t)r * HD * 2);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + base, (uint32_t)r * HD * 2);
+    const int64_t qbase = ((int64_t)(s.q0 + row0) * a.H + h) * D;
+    const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qbase, (uint32_t)r * HD * 2);
+
+    __builtin_amdgcn_wave_barrier();
+    load_tile_async<D>(kt, rk, 0, HD, lane, 0, 1);
+    load_tile_async<D>(vt, rv, 0, HD, lane, 0, 1);
+    bf16x8 qf[2][NKK];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        qf[qb][kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)((qb * 32 + l32) * HD + kk * 16 + g * 8) * 2));
+    wait_vmem();
+    __builtin_amdgcn_wave_barrier();
+
+    // S^T[kb][qb]
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = row_frag<D>(kt, kb * 32 + l32, kk, g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = Elem<bf16>::mma(kf, qf[qb][kk], sacc[kb][qb]);
+      }
+
+    const int npad = 64 - r;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[kb][qb][i] *= a.scale_log2;
+          mx = fmaxf(mx, sacc[kb][qb][i]);
+        }
+      mx = wave_xor32_max(mx);
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = round_p<bf16>(exp2f(sacc[kb][qb][i] - mx));
+          sacc[kb][qb][i] = e;
+          ls += e;
+        }
+      ls = wave_xor32_sum(ls) - (float)npad * round_p<bf16>(exp2f(-mx));
+      const float inv = 1.0f / ls;
+      f32x16 oacc[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 pf = pack8_from(sacc[kb][qb], st * 8);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) oacc[d] = Elem<bf16>::mma(tr_frag<D>(vt, kb, st, d * 32, lane), pf, oacc[d]);
+        }
+      const int row = qb * 32 + l32;
+      if (row < r) {
+        TO* orow = reinterpret_cast<TO*>(a.o) + qbase + (int64_t)row * HD;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            store4<TO>(orow + d * 32 + i4 * 8 + g * 4, oacc[d][i4 * 4] * inv, oacc[d][i4 * 4 + 1] * inv,
+                       oacc[d][i4 * 4 + 2] * inv, oacc[d][i4 * 4 + 3] * inv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward: a wave pair per block, two pairs per workgroup in lockstep
+// ---------------------------------------------------------------------------
+template <typename TG, int D>
+__global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
+  using T = Tile<D>;
+  constexpr int NKK = D / 16, ND = D / 32;
+  constexpr int PAIR_BYTES = 4 * T::BYTES + 2 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * PAIR_BYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int pair = wave >> 1, w2 = wave & 1;
+  char* qt = smem + pair * PAIR_BYTES;
+  char* kt = qt + T::BYTES;
+  char* vt = kt + T::BYTES;
+  char* ot = vt + T::BYTES;  // dO
+  float* L2s = reinterpret_cast<float*>(ot + T::BYTES);
+  float* Dis = L2s + 64;
+  // each wave pair walks its own worker list; the two pairs of a workgroup
+  // run the same number of rounds so that every barrier is reached by all
+  const int wbase = xcd_worker(blockIdx.x, gridDim.x) * 2;
+  const int u0 = a.worker_off[wbase + pair], u1 = a.worker_off[wbase + pair + 1];
+  const int rounds = max(a.worker_off[wbase + 1] - a.worker_off[wbase], a.worker_off[wbase + 2] - a.worker_off[wbase + 1]);
+  const int HD = a.H * D;
+
+  for (int k = 0; k < rounds; ++k) {
+    const int u = u0 + k;
+    const bool active = u < u1;
+    int r = 0;
+    int64_t qbase = 0, kbase = 0;
+    if (active) {
+      const i32x4 unit = reinterpret_cast<const i32x4*>(a.units)[u];
+      const int b = unit[0], h = unit[1], t = unit[2];
+      const Sample s = load_sample(a.samples, b);
+      const int row0 = t * 64;
+      r = min(64, s.lq - row0);
+      qbase = ((int64_t)(s.q0 + row0) * a.H + h) * D;
+      kbase = ((int64_t)(s.k0 + row0) * a.H + h) * D;
+      const uint32_t nbytes = (uint32_t)r * HD * 2;
+      const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qbase, nbytes);
+      const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kbase, nbytes);
+      const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kbase, nbytes);
+      const rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qbase, nbytes);
+      load_tile_async<D>(qt, rq, 0, HD, lane, w2, 2);
+      load_tile_async<D>(kt, rk, 0, HD, lane, w2, 2);
+      load_tile_async<D>(vt, rv, 0, HD, lane, w2, 2);
+      load_tile_async<D>(ot, ro, 0, HD, lane, w2, 2);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    const int npad = 64 - r;
+    // ---- phase 1: lane = query row (w2*32 + l32) ----
+    if (active) {
+      bf16x8 qf[NKK], of[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        qf[kk] = row_frag<D>(qt, w2 * 32 + l32, kk, g);
+        of[kk] = row_frag<D>(ot, w2 * 32 + l32, kk, g);
+      }
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        dpacc[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc[kb] = Elem<bf16>::mma(row_frag<D>(kt, kb * 32 + l32, kk, g), qf[kk], sacc[kb]);
+          dpacc[kb] = Elem<bf16>::mma(row_frag<D>(vt, kb * 32 + l32, kk, g), of[kk], dpacc[kb]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[kb][i] *= a.scale_log2;
+          mx = fmaxf(mx, sacc[kb][i]);
+        }
+      mx = wave_xor32_max(mx);
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = exp2f(sacc[kb][i] - mx);
+          sacc[kb][i] = e;
+          ls += e;
+        }
+      ls = wave_xor32_sum(ls) - (float)npad * exp2f(-mx);
+      const float inv = 1.0f / ls;
+      // Di = sum_j P_ij dP_ij over the block's keys (tail keys have dP = 0)
+      float di = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[kb][i] *= inv;  // P
+          di += sacc[kb][i] * dpacc[kb][i];
+        }
+      di = wave_xor32_sum(di);
+      float ds[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[kb][i] = sacc[kb][i] * (dpacc[kb][i] - di);
+      if (g == 0) {
+        L2s[w2 * 32 + l32] = mx + __log2f(ls);
+        Dis[w2 * 32 + l32] = di;
+      }
+      f32x16 dqacc[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) dqacc[d] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 df = pack8(&ds[kb][st * 8]);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) dqacc[d] = Elem<bf16>::mma(tr_frag<D>(kt, kb, st, d * 32, lane), df, dqacc[d]);
+        }
+      const int row = w2 * 32 + l32;
+      if (row < r) {
+        TG* grow = reinterpret_cast<TG*>(a.dq) + qbase + (int64_t)row * HD;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            store4<TG>(grow + d * 32 + i4 * 8 + g * 4, dqacc[d][i4 * 4] * a.scale, dqacc[d][i4 * 4 + 1] * a.scale,
+                       dqacc[d][i4 * 4 + 2] * a.scale, dqacc[d][i4 * 4 + 3] * a.scale);
+      }
+    }
+    __syncthreads();
+
+    // ---- phase 2: lane = key row (w2*32 + l32) ----
+    if (active) {
+      bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        kf[kk] = row_frag<D>(kt, w2 * 32 + l32, kk, g);
+        vf[kk] = row_frag<D>(vt, w2 * 32 + l32, kk, g);
+      }
+      f32x16 dkacc[ND], dvacc[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        dkacc[d] = f32x16{};
+        dvacc[d] = f32x16{};
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc = Elem<bf16>::mma(row_frag<D>(qt, qb * 32 + l32, kk, g), kf[kk], sacc);
+          dpacc = Elem<bf16>::mma(row_frag<D>(ot, qb * 32 + l32, kk, g), vf[kk], dpacc);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = qb * 32 + acc_row(i, g);
+          p[i] = exp2f(sacc[i] * a.scale_log2 - L2s[q]);
+          ds[i] = p[i] * (dpacc[i] - Dis[q]);
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 pf = pack8(&p[st * 8]);
+          const bf16x8 df = pack8(&ds[st * 8]);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            dvacc[d] = Elem<bf16>::mma(tr_frag<D>(ot, qb, st, d * 32, lane), pf, dvacc[d]);
+            dkacc[d] = Elem<bf16>::mma(tr_frag<D>(qt, qb, st, d * 32, lane), df, dkacc[d]);
+          }
+        }
+      }
+      const int row = w2 * 32 + l32;
+      if (row < r) {
+        TG* krp = reinterpret_cast<TG*>(a.dk) + kbase + (int64_t)row * HD;
+        TG* vrp = reinterpret_cast<TG*>(a.dv) + kbase + (int64_t)row * HD;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int col = d * 32 + i4 * 8 + g * 4;
+            store4<TG>(krp + col, dkacc[d][i4 * 4] * a.scale, dkacc[d][i4 * 4 + 1] * a.scale,
+                       dkacc[d][i4 * 4 + 2] * a.scale, dkacc[d][i4 * 4 + 3] * a.scale);
+            store4<TG>(vrp + col, dvacc[d][i4 * 4], dvacc[d][i4 * 4 + 1], dvacc[d][i4 * 4 + 2], dvacc[d][i4 * 4 + 3]);
+          }
+      }
+    }
+    __syncthreads();  // tiles are reloaded next round
+  }
+}
+
+}  // namespace jattn

@@ -110,5 +110,9 @@ hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_
 hipError_t launch_dq(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_t st);
+// BlockAttention: grid = number of workgroups; each workgroup runs two
+// workers (wave pairs) of the block plan.
+hipError_t launch_block_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+hipError_t launch_block_bwd(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 
 }  // namespace jattn

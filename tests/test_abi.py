@@ -73,6 +73,10 @@ def _desc(**kw):
     (dict(want_dbias=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
     (dict(order=9), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
     (dict(mask=B.JATTN_MASK_BLOCKDIAG64, act=B.JATTN_GELU_ERF), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(mask=B.JATTN_MASK_BLOCKDIAG64, has_bias=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(mask=B.JATTN_MASK_BLOCKDIAG64, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
+     [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(mask=B.JATTN_MASK_BLOCKDIAG64, num_workers=7), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
 ])
 def test_plan_create_rejects(lib, kw, qo, ko, code):
     d = _desc(**kw)
@@ -179,6 +183,8 @@ def test_random_plans_match(lib, seed):
     qo, ko = gen.offsets_from_lengths(lq), gen.offsets_from_lengths(lk)
     W = int(rng.integers(1, 50))
     block = seed % 2 == 0 and seed % 4 == 0
+    if block:
+        W += W % 2  # block plans run two workers per workgroup
     for order in range(3):
         d = _desc(B=Bn, H=3, D=64, order=order, num_workers=W, mask=1 if block else 0)
         p = B.jattn_plan_create(d, qo, ko)
