@@ -1,0 +1,266 @@
+"""Benchmark: jagged attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path (forward, then the backward's Di,
+dK/dV and dQ stages, or the fused block kernels) over one batch of seeded
+synthetic inputs that are resident in HBM before timing starts.  The value is
+fwd+bwd TFLOP/s counted over valid (unpadded) tokens only:
+    FLOPs_fwd = 4 H D sum_b lq_b lk_b        FLOPs_bwd = 2.5 FLOPs_fwd
+Every launch is also timed with HIP events on the stream it runs on; the
+kernel with the largest share gets a roofline entry.  The fp64 CPU oracle is
+timed beside it on a bounded sample of the same workload (first samples in
+order, fwd+bwd) as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (1 = headline)")
+    ap.add_argument("--order", default="heavy_first")
+    ap.add_argument("--workers", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    return ap.parse_args()
+
+
+def kernel_work(w, info, es_in, es_out, es_g):
+    """Algorithmic bytes and FLOPs of each launch (every interface tensor once)."""
+    H, D = w.H, w.D
+    Tq, Tk, nb = int(info.Tq), int(info.Tk), int(info.bias_elems)
+    qd, kd = Tq * H * D, Tk * H * D
+    F = float(info.flops_fwd)
+    bias_in = nb * es_in if w.bias else 0
+    dbias_out = nb * es_g if w.want_dbias else 0
+    rowstat = Tq * H * 4
+    if w.block_diagonal:
+        return {
+            "block_fwd": (3 * qd * es_in + qd * es_out, F),
+            "block_bwd": (4 * qd * es_in + 3 * qd * es_g, 2.5 * F),
+        }
+    soft = w.act == "softmax"
+    work = {
+        "fwd": (qd * es_in + 2 * kd * es_in + bias_in + qd * es_out + (rowstat if soft else 0), F),
+        "dkdv": (2 * qd * es_in + 2 * kd * es_in + bias_in + (2 * rowstat if soft else 0)
+                 + 2 * kd * es_g + dbias_out, 2.0 * F),
+        "dq": (2 * qd * es_in + 2 * kd * es_in + bias_in + (2 * rowstat if soft else 0) + qd * es_g, 0.5 * F),
+    }
+    if soft:
+        work["prep"] = (qd * es_out + qd * es_in + rowstat, 2.0 * qd)
+    return work
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "jagged_variable_length_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s):
+    """fp64 oracle, fwd+bwd, samples in order until the time budget is spent."""
+    from oracle import attention as ora
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        cores = None
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    do, bias = inp.f64("dout"), inp.f64("bias")
+    scale = 1.0 / np.sqrt(w.D)
+    # warm-up on a small sample
+    ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, 0, scale=scale, activation=w.act,
+                       block_diagonal=w.block_diagonal, bias=bias)
+    lq, lk = inp.lq, inp.lk
+    flops, n = 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(inp.B):
+        ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
+                           block_diagonal=w.block_diagonal, bias=bias)
+        ora.backward_sample(q, k, v, do, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
+                            block_diagonal=w.block_diagonal, bias=bias, want_dbias=w.want_dbias)
+        if w.block_diagonal:
+            pairs = sum(min(64, int(lq[b]) - s) ** 2 for s in range(0, int(lq[b]), 64))
+        else:
+            pairs = int(lq[b]) * int(lk[b])
+        flops += 3.5 * 4.0 * w.H * w.D * pairs
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs (--gpus > 1) are not supported "
+              "(attention has no cross-GPU exchange; the sharding design is per-sample data parallel)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from jagged_variable_length_amd import attention as A
+    from jagged_variable_length_amd import binding as Bd
+    from jagged_variable_length_amd import inputs as gen
+
+    cfg = args.config
+    w = gen.WORKLOADS[cfg]
+    inp = gen.make_inputs(cfg, cfg)
+    op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
+                           has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
+                           grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
+                           num_workers=args.workers)
+    t0 = time.perf_counter()
+    plan_ms = None
+    op.upload()
+    dev = {n: A.to_device(getattr(inp, n), w.dtype) for n in ("q", "k", "v", "dout")}
+    bias = A.to_device(inp.bias, w.dtype) if inp.bias is not None else None
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    o = torch.empty(op.Tq, w.H, w.D, dtype=tdt[w.out_dtype], device="cuda")
+    lse = torch.empty(op.Tq, w.H, dtype=torch.float32, device="cuda") if (w.act == "softmax" and not w.block_diagonal) else None
+    dq = torch.empty(op.Tq, w.H, w.D, dtype=tdt[w.grad_dtype], device="cuda")
+    dk = torch.empty(op.Tk, w.H, w.D, dtype=tdt[w.grad_dtype], device="cuda")
+    dv = torch.empty_like(dk)
+    dbias = torch.empty(int(op.info.bias_elems), dtype=tdt[w.grad_dtype], device="cuda") if w.want_dbias else None
+    torch.cuda.synchronize()
+    # plan creation cost (host only), measured on a fresh plan
+    t1 = time.perf_counter()
+    p2 = Bd.jattn_plan_create(op.desc, inp.q_offsets, inp.kv_offsets)
+    plan_ms = (time.perf_counter() - t1) * 1e3
+    Bd.jattn_plan_destroy(p2)
+
+    if w.block_diagonal:
+        launches = [("block_fwd", lambda: op.forward(dev["q"], dev["k"], dev["v"], o=o)),
+                    ("block_bwd", lambda: op.backward(dev["q"], dev["k"], dev["v"], dev["dout"], dq=dq, dk=dk, dv=dv))]
+    else:
+        def fwd():
+            op.forward(dev["q"], dev["k"], dev["v"], bias=bias, o=o, lse=lse)
+
+        def stage(s):
+            return lambda: op.backward(dev["q"], dev["k"], dev["v"], dev["dout"], o=o, lse=lse, bias=bias,
+                                       dq=dq, dk=dk, dv=dv, dbias=dbias, stages=s)
+        launches = [("fwd", fwd)]
+        if w.act == "softmax":
+            launches.append(("prep", stage(Bd.JATTN_BWD_PREP)))
+        launches += [("dkdv", stage(Bd.JATTN_BWD_DKDV)), ("dq", stage(Bd.JATTN_BWD_DQ))]
+
+    for _ in range(args.warmup):
+        for _, f in launches:
+            f()
+    torch.cuda.synchronize()
+
+    ev = {n: [] for n, _ in launches}
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        for n, f in launches:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in lst])) for n, lst in ev.items()}
+
+    F = float(op.info.flops_fwd)
+    total_flops = 3.5 * F
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+
+    es = {"bf16": 2, "f32": 4}
+    work = kernel_work(w, op.info, es[w.dtype], es[w.out_dtype], es[w.grad_dtype])
+    dom = max(ms, key=lambda n: ms[n])
+    nbytes, nflops = work[dom]
+    t = ms[dom] * 1e-3
+    ridge = peak / (PEAK_HBM_GBS / 1e3)
+    if nflops / nbytes < ridge:
+        achieved = nbytes / t / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = nflops / t / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+    roof["traffic"] = traffic_for(dom)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+    roof["ms_per_launch"] = ms[dom]
+
+    kernels = {}
+    for n in ms:
+        b_, f_ = work[n]
+        kernels[n] = {"ms": round(ms[n], 4), "GB/s": round(b_ / (ms[n] * 1e-3) / 1e9, 1),
+                      "TFLOP/s": round(f_ / (ms[n] * 1e-3) / 1e12, 2)}
+
+    out = {
+        "metric": "jagged attn fwd+bwd TFLOPs (valid tokens) and % of bf16 MFMA peak, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; lengths and value distributions of the workload)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} D={w.D} {w.dtype} act={w.act}"
+                               f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}",
+                   "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk, "seed": cfg,
+                   "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),
+                   "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype},
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

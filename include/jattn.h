@@ -165,6 +165,22 @@ int jattn_bwd(const jattn_plan* plan, const void* q, const void* k, const void* 
               const void* bias, const void* o, const float* lse, const void* dout, void* dq,
               void* dk, void* dv, void* dbias, void* workspace, void* stream);
 
+/* Backward stages (bit mask for jattn_bwd_stages). */
+#define JATTN_BWD_PREP 1 /* Di = rowsum(dO * O) into the workspace (softmax, mask NONE) */
+#define JATTN_BWD_DKDV 2 /* dK, dV (and dBias) */
+#define JATTN_BWD_DQ 4   /* dQ */
+#define JATTN_BWD_ALL 7
+
+/* Same as jattn_bwd but runs only the stages in `stages`.  PREP must have
+ * completed (on this or an ordered stream) before DKDV or DQ run; DKDV and
+ * DQ are independent of each other and may run concurrently on two streams
+ * (they write disjoint outputs and only read the workspace).  Block mode has
+ * a single fused stage, run when DKDV or DQ is requested. */
+int jattn_bwd_stages(const jattn_plan* plan, int32_t stages, const void* q, const void* k,
+                     const void* v, const void* bias, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* dbias, void* workspace,
+                     void* stream);
+
 void jattn_plan_destroy(jattn_plan* plan);
 
 /* Static text for a status code. */

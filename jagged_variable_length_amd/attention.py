@@ -84,7 +84,8 @@ class JaggedAttention:
                      self.workspace.data_ptr(), self._stream())
         return o, lse
 
-    def backward(self, q, k, v, dout, o=None, lse=None, bias=None, dq=None, dk=None, dv=None, dbias=None):
+    def backward(self, q, k, v, dout, o=None, lse=None, bias=None, dq=None, dk=None, dv=None, dbias=None,
+                 stages=_b.JATTN_BWD_ALL):
         if self.workspace is None:
             self.upload()
         gdt = _TORCH_DT[self.grad_dtype]
@@ -93,8 +94,12 @@ class JaggedAttention:
         dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         if self.want_dbias and dbias is None:
             dbias = torch.empty(int(self.info.bias_elems), dtype=gdt, device=self.device)
-        _b.jattn_bwd(self.plan, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout),
-                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
+        if stages == _b.JATTN_BWD_ALL:
+            _b.jattn_bwd(self.plan, *args)
+        else:
+            _b.jattn_bwd_stages(self.plan, stages, *args)
         return dq, dk, dv, dbias
 
     def __del__(self):

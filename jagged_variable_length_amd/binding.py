@@ -23,8 +23,11 @@ JATTN_BF16, JATTN_F32 = 0, 1
 JATTN_HEAVY_FIRST, JATTN_ZIGZAG, JATTN_LPT = 0, 1, 2
 JATTN_PLAN_FWD, JATTN_PLAN_DKDV, JATTN_PLAN_DQ, JATTN_PLAN_BLOCK = 0, 1, 2, 3
 
+JATTN_BWD_PREP, JATTN_BWD_DKDV, JATTN_BWD_DQ, JATTN_BWD_ALL = 1, 2, 4, 7
+
 EXPORTED = ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
-            "jattn_fwd", "jattn_bwd", "jattn_plan_destroy", "jattn_strerror", "jattn_last_error"]
+            "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_plan_destroy", "jattn_strerror",
+            "jattn_last_error"]
 
 
 class JattnError(RuntimeError):
@@ -74,6 +77,7 @@ def lib():
     L.jattn_plan_upload.argtypes = [vp, vp, i64, vp]
     L.jattn_fwd.argtypes = [vp] * 9
     L.jattn_bwd.argtypes = [vp] * 14
+    L.jattn_bwd_stages.argtypes = [vp, i32] + [vp] * 13
     L.jattn_plan_destroy.argtypes = [vp]
     L.jattn_plan_destroy.restype = None
     L.jattn_strerror.argtypes = [ctypes.c_int]
@@ -81,7 +85,7 @@ def lib():
     L.jattn_last_error.argtypes = []
     L.jattn_last_error.restype = ctypes.c_char_p
     for name in ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
-                 "jattn_fwd", "jattn_bwd"]:
+                 "jattn_fwd", "jattn_bwd", "jattn_bwd_stages"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -131,6 +135,10 @@ def jattn_fwd(plan, q, k, v, bias, o, lse, workspace, stream) -> None:
 
 def jattn_bwd(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
     _check(lib().jattn_bwd(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
+
+
+def jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
+    _check(lib().jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
 
 
 def jattn_plan_destroy(plan: int) -> None:

@@ -324,7 +324,14 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
 int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias, const void* o,
               const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* workspace,
               void* stream) {
+  return jattn_bwd_stages(p, JATTN_BWD_ALL, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream);
+}
+
+int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const void* k, const void* v,
+                     const void* bias, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                     void* dv, void* dbias, void* workspace, void* stream) {
   if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (stages < 0 || stages > JATTN_BWD_ALL) return fail(JATTN_E_ARG, "unknown backward stage mask");
   if (p->Tq == 0 && p->Tk == 0) return ok();
   const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask == JATTN_MASK_NONE;
   if ((p->Tq > 0 && (!q || !dout || !dq)) || (p->Tk > 0 && (!k || !v || !dk || !dv)))
@@ -350,7 +357,7 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   sel.wkv = p->dkdv_wkv;
   hipError_t e;
   if (p->desc.mask == JATTN_MASK_BLOCKDIAG64) {
-    if (p->block.n_units() == 0) return ok();
+    if (p->block.n_units() == 0 || !(stages & (JATTN_BWD_DKDV | JATTN_BWD_DQ))) return ok();
     jattn::BwdArgs a{};
     a.q = q;
     a.k = k;
@@ -369,7 +376,7 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
     if (e != hipSuccess) return hip_fail(e, "block backward launch");
     return ok();
   }
-  if (softmax_dense && p->Tq > 0) {
+  if (softmax_dense && p->Tq > 0 && (stages & JATTN_BWD_PREP)) {
     jattn::DiArgs da{o, dout, di, p->Tq * p->H};
     e = jattn::launch_di(da, sel, p->desc.out_dtype == JATTN_F32, st);
     if (e != hipSuccess) return hip_fail(e, "Di launch");
@@ -390,13 +397,13 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   a.H = p->H;
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.4426950408889634f;
-  if (p->dkdv.n_units() > 0) {
+  if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
     a.units = ws_ptr(workspace, p->off_dkdv_u);
     a.worker_off = ws_ptr(workspace, p->off_dkdv_o);
     e = jattn::launch_dkdv(a, sel, p->dkdv.num_workers, st);
     if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
   }
-  if (p->dq.n_units() > 0) {
+  if (p->dq.n_units() > 0 && (stages & JATTN_BWD_DQ)) {
     a.units = ws_ptr(workspace, p->off_dq_u);
     a.worker_off = ws_ptr(workspace, p->off_dq_o);
     e = jattn::launch_dq(a, sel, p->dq.num_workers, st);
