@@ -44,14 +44,14 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(w, info, es_in, es_out, es_g):
+def kernel_work(w, info, es_in, es_out, es_g, es_db=4):
     """Algorithmic bytes and FLOPs of each launch (every interface tensor once)."""
     H, D = w.H, w.D
     Tq, Tk, nb = int(info.Tq), int(info.Tk), int(info.bias_elems)
     qd, kd = Tq * H * D, Tk * H * D
     F = float(info.flops_fwd)
     bias_in = nb * es_in if w.bias else 0
-    dbias_out = nb * es_g if w.want_dbias else 0
+    dbias_out = nb * es_db if w.want_dbias else 0
     rowstat = Tq * H * 4
     if w.block_diagonal:
         return {
@@ -149,7 +149,7 @@ def main():
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
                            has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
-                           num_workers=args.workers)
+                           num_workers=args.workers, dbias_dtype=w.dbias_dtype)
     t0 = time.perf_counter()
     plan_ms = None
     op.upload()
@@ -161,7 +161,7 @@ def main():
     dq = torch.empty(op.Tq, w.H, w.D, dtype=tdt[w.grad_dtype], device="cuda")
     dk = torch.empty(op.Tk, w.H, w.D, dtype=tdt[w.grad_dtype], device="cuda")
     dv = torch.empty_like(dk)
-    dbias = torch.empty(int(op.info.bias_elems), dtype=tdt[w.grad_dtype], device="cuda") if w.want_dbias else None
+    dbias = torch.empty(int(op.info.bias_elems), dtype=tdt[w.dbias_dtype], device="cuda") if w.want_dbias else None
     torch.cuda.synchronize()
     # plan creation cost (host only), measured on a fresh plan
     t1 = time.perf_counter()
@@ -210,7 +210,7 @@ def main():
     peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
 
     es = {"bf16": 2, "f32": 4}
-    work = kernel_work(w, op.info, es[w.dtype], es[w.out_dtype], es[w.grad_dtype])
+    work = kernel_work(w, op.info, es[w.dtype], es[w.out_dtype], es[w.grad_dtype], es[w.dbias_dtype])
     dom = max(ms, key=lambda n: ms[n])
     nbytes, nflops = work[dom]
     t = ms[dom] * 1e-3
@@ -252,7 +252,8 @@ def main():
                                f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}",
                    "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk, "seed": cfg,
                    "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),
-                   "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype},
+                   "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype,
+                   "dbias_dtype": w.dbias_dtype if w.want_dbias else None},
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": None,

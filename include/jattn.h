@@ -97,11 +97,12 @@ typedef struct {
   int32_t want_dbias;   /* 0/1: backward writes dBias (needs has_bias) */
   int32_t in_dtype;     /* q, k, v, bias, dout: JATTN_BF16 | JATTN_F32 */
   int32_t out_dtype;    /* o */
-  int32_t grad_dtype;   /* dq, dk, dv, dbias */
+  int32_t grad_dtype;   /* dq, dk, dv */
   int32_t split_operands; /* 0/1: P and dS enter the PV-type products as
                              bf16 hi + lo pairs (two MFMAs) for accuracy */
   int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
-  int32_t num_workers;  /* persistent workgroups per kernel; 0 = default */
+  int32_t num_workers;  /* persistent workers per kernel; 0 = default */
+  int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
 } jattn_desc;
 
 /* Per-kernel plan figures.  tile_rows: rows of the unit's own tile (q rows
@@ -154,7 +155,7 @@ int jattn_fwd(const jattn_plan* plan, const void* q, const void* k, const void* 
               const void* bias, void* o, float* lse, void* workspace, void* stream);
 
 /* Backward.  Given dout, writes dq, dk, dv (grad_dtype) and, if
- * desc.want_dbias, dbias (grad_dtype).  Softmax with mask NONE needs o and
+ * desc.want_dbias, dbias (dbias_dtype).  Softmax with mask NONE needs o and
  * the forward's lse (JATTN_E_STATE otherwise); GDPA needs neither; block
  * mode recomputes its row statistics in-tile and needs neither.  Uses the
  * workspace's scratch region for row statistics.  No atomics: every output

@@ -34,7 +34,7 @@ class JaggedAttention:
                  in_dtype: str = "bf16", out_dtype: Optional[str] = None,
                  grad_dtype: Optional[str] = None, split_operands: bool = False,
                  order: str = "heavy_first", num_workers: int = 0, scale: Optional[float] = None,
-                 device="cuda"):
+                 dbias_dtype: Optional[str] = None, device="cuda"):
         q_offsets = np.asarray(q_offsets, dtype=np.int64)
         kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
         self.B = len(q_offsets) - 1
@@ -43,6 +43,7 @@ class JaggedAttention:
         self.in_dtype = in_dtype
         self.out_dtype = out_dtype or in_dtype
         self.grad_dtype = grad_dtype or in_dtype
+        self.dbias_dtype = dbias_dtype or self.grad_dtype
         self.has_bias, self.want_dbias = has_bias, want_dbias
         self.block_diagonal = block_diagonal
         self.scale = (1.0 / math.sqrt(D)) if scale is None else scale
@@ -56,6 +57,7 @@ class JaggedAttention:
         d.split_operands = int(split_operands)
         d.order = _ORDER[order]
         d.num_workers = num_workers
+        d.dbias_dtype = _DT[self.dbias_dtype]
         self.desc = d
         self.plan = _b.jattn_plan_create(d, q_offsets, kv_offsets)
         self.info = _b.jattn_plan_info(self.plan)
@@ -93,7 +95,7 @@ class JaggedAttention:
         dk = dk if dk is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         if self.want_dbias and dbias is None:
-            dbias = torch.empty(int(self.info.bias_elems), dtype=gdt, device=self.device)
+            dbias = torch.empty(int(self.info.bias_elems), dtype=_TORCH_DT[self.dbias_dtype], device=self.device)
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                 _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
         if stages == _b.JATTN_BWD_ALL:

@@ -42,7 +42,8 @@ class jattn_desc(ctypes.Structure):
                 ("has_bias", ctypes.c_int32), ("want_dbias", ctypes.c_int32),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("split_operands", ctypes.c_int32),
-                ("order", ctypes.c_int32), ("num_workers", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("num_workers", ctypes.c_int32),
+                ("dbias_dtype", ctypes.c_int32)]
 
 
 class jattn_kernel_plan(ctypes.Structure):

@@ -67,6 +67,7 @@ KernelSel base_sel(const jattn_plan* p) {
   k.act = p->desc.act;
   k.bias = p->desc.has_bias != 0;
   k.dbias = p->desc.want_dbias != 0;
+  k.dbias_f32 = p->desc.dbias_dtype == JATTN_F32;
   k.split = p->desc.split_operands != 0;
   k.in_f32 = p->desc.in_dtype == JATTN_F32;
   return k;
@@ -116,6 +117,7 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   if (d.in_dtype != JATTN_BF16 && d.in_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown in_dtype");
   if (d.out_dtype != JATTN_BF16 && d.out_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown out_dtype");
   if (d.grad_dtype != JATTN_BF16 && d.grad_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown grad_dtype");
+  if (d.dbias_dtype != JATTN_BF16 && d.dbias_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown dbias_dtype");
   if (d.in_dtype == JATTN_F32 && (d.out_dtype != JATTN_F32 || d.grad_dtype != JATTN_F32))
     return fail(JATTN_E_UNSUPPORTED, "fp32 inputs need fp32 outputs and gradients");
   if (d.in_dtype == JATTN_F32 && d.D > 64) return fail(JATTN_E_UNSUPPORTED, "fp32 inputs support D <= 64");
@@ -345,7 +347,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
       !aligned(dk, 16) || !aligned(dv, 16) || !aligned(o, 16))
     return fail(JATTN_E_ALIGN, "value tensors must be 16-byte aligned");
   const int es = elem_size(p->desc.in_dtype);
-  if ((bias && !aligned(bias, (uintptr_t)es)) || (dbias && !aligned(dbias, (uintptr_t)elem_size(p->desc.grad_dtype))))
+  if ((bias && !aligned(bias, (uintptr_t)es)) || (dbias && !aligned(dbias, (uintptr_t)elem_size(p->desc.dbias_dtype))))
     return fail(JATTN_E_ALIGN, "bias/dbias must be element-aligned");
   if (lse && !aligned(lse, 4)) return fail(JATTN_E_ALIGN, "lse must be 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);

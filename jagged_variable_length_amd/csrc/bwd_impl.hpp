@@ -18,6 +18,8 @@
 // the row index (K for dQ; Q and dO for dK/dV) are staged transposed in LDS
 // with the 32-block permutation that matches the MFMA accumulator layout.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
@@ -328,7 +330,8 @@ struct DkdvShape {
   static_assert(kThreads % KT == 0, "bias staging assumes KT | 256");
 };
 
-template <typename TI, typename TG, int D, int WKV, int ACT, bool BIAS, bool DBIAS, bool SPLIT>
+// DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
+template <typename TI, typename TG, int D, int WKV, int ACT, bool BIAS, int DBIAS, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   using E = Elem<TI>;
   using Sh = DkdvShape<TI, D, WKV>;
@@ -512,11 +515,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       if constexpr (DBIAS) {
         const int kv = kt * KT + kvl;
         if (kv < s.lk) {
-          TG* db = reinterpret_cast<TG*>(a.dbias) + bias_hb + kv;
+          typedef typename std::conditional<DBIAS == 2, float, bf16>::type TB;
+          TB* db = reinterpret_cast<TB*>(a.dbias) + bias_hb + kv;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int q = t * QS + wqs * 32 + acc_row(i, g);
-            if (q < s.lq) db[(int64_t)q * s.lk] = (TG)ds[i];
+            if (q < s.lq) db[(int64_t)q * s.lk] = (TB)ds[i];
           }
         }
       }

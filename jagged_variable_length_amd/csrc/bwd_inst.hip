@@ -38,7 +38,7 @@ hipError_t dq_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t 
   return dq_act<TI, TG, D, WQ, WK, kSilu>(a, k, grid, st);
 }
 
-template <typename TI, typename TG, int D, int WKV, int ACT, bool BIAS, bool DBIAS, bool SPLIT>
+template <typename TI, typename TG, int D, int WKV, int ACT, bool BIAS, int DBIAS, bool SPLIT>
 hipError_t dkdv_one(const BwdArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL((dkdv_kernel<TI, TG, D, WKV, ACT, BIAS, DBIAS, SPLIT>), dim3(grid), dim3(kThreads), 0,
                      st, a);
@@ -48,10 +48,11 @@ hipError_t dkdv_one(const BwdArgs& a, int grid, hipStream_t st) {
 template <typename TI, typename TG, int D, int WKV, int ACT, bool SPLIT>
 hipError_t dkdv_bias(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.bias) {
-    if (k.dbias) return dkdv_one<TI, TG, D, WKV, ACT, true, true, SPLIT>(a, grid, st);
-    return dkdv_one<TI, TG, D, WKV, ACT, true, false, SPLIT>(a, grid, st);
+    if (k.dbias && k.dbias_f32) return dkdv_one<TI, TG, D, WKV, ACT, true, 2, SPLIT>(a, grid, st);
+    if (k.dbias) return dkdv_one<TI, TG, D, WKV, ACT, true, 1, SPLIT>(a, grid, st);
+    return dkdv_one<TI, TG, D, WKV, ACT, true, 0, SPLIT>(a, grid, st);
   }
-  return dkdv_one<TI, TG, D, WKV, ACT, false, false, SPLIT>(a, grid, st);
+  return dkdv_one<TI, TG, D, WKV, ACT, false, 0, SPLIT>(a, grid, st);
 }
 
 template <typename TI, typename TG, int D, int WKV, int ACT>

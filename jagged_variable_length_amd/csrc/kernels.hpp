@@ -61,6 +61,7 @@ struct KernelSel {
   int act;        // 0 softmax, 1 gelu, 2 silu
   bool bias;      // additive bias input
   bool dbias;     // write dBias
+  bool dbias_f32; // dBias element type is fp32 (else bf16)
   bool split;     // hi/lo bf16 operands for P / dS products
   bool in_f32;    // inputs are fp32 (else bf16)
   bool out_f32;   // O (fwd) or dQ/dK/dV (bwd) are fp32 (else bf16)

@@ -45,6 +45,7 @@ class Workload:
     out_dtype: str
     grad_dtype: str
     split_operands: bool
+    dbias_dtype: str = "f32"
 
 
 WORKLOADS = {

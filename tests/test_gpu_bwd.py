@@ -100,7 +100,7 @@ def test_bwd_bf16_gradients_balanced():
     rng = np.random.default_rng(3)
     lens = np.clip(np.rint(np.exp(np.log(300) + rng.standard_normal(12))), 8, 1000).astype(int)
     inp = gen.make_custom(lens, lens, 4, 128, "bf16", seed=3, bias=True)
-    op, got, _ = _run(inp, bias=True, want_dbias=True)
+    op, got, _ = _run(inp, bias=True, want_dbias=True, dbias_dtype="bf16")
     _compare(inp, op, got)
 
 
