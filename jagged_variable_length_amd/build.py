@@ -27,14 +27,18 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
 # (source, object name, extra defines)
+# (D, input type, output/gradient type) instances of the fp32 forward and the backward
 FWD_INST = [(128, "bf16", "bf16"), (128, "bf16", "f32"), (64, "bf16", "bf16"), (64, "bf16", "f32"),
             (64, "f32", "f32"), (32, "bf16", "bf16"), (32, "bf16", "f32"), (32, "f32", "f32")]
 
 
 def units():
     u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", [])]
+    for d in (128, 64, 32):
+        u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
     for d, ti, to in FWD_INST:
-        u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
+        if ti == "f32":
+            u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
         di = ["-DJ_DI"] if ti == to else []  # Di launcher once per (D, dO type)
         u.append(("bwd_inst.hip", f"bwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TG={to}"] + di))
     return u

@@ -201,13 +201,16 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     // Query-tile shape: 4 waves x 32 rows, or (short queries) one 32-row
     // group whose key tiles are split over the 4 waves.
     p->fwd_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
-    p->dq_wq = p->fwd_wq;
+    // the bf16 short-query forward has no room for a bias tile at D = 128
+    if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias) p->fwd_wq = 4;
+    p->dq_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
     const int fwd_tile = 32 * p->fwd_wq, fwd_step = p->fwd_wq == 4 ? 64 : 128;
+    const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
     const int dkdv_tile = 32 * p->dkdv_wkv, dkdv_step = 32 * (4 / p->dkdv_wkv);
     jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd);
-    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->dq);
+    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq);
     jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, W, order, &p->dkdv);
   }
   append(p->image, p->fwd, &p->off_fwd_u, &p->off_fwd_o);
@@ -425,14 +428,9 @@ hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_
     if (k.D == 64) return launch_fwd_64_f32_f32(a, k, grid, st);
     return launch_fwd_32_f32_f32(a, k, grid, st);
   }
-  if (k.out_f32) {
-    if (k.D == 128) return launch_fwd_128_bf16_f32(a, k, grid, st);
-    if (k.D == 64) return launch_fwd_64_bf16_f32(a, k, grid, st);
-    return launch_fwd_32_bf16_f32(a, k, grid, st);
-  }
-  if (k.D == 128) return launch_fwd_128_bf16_bf16(a, k, grid, st);
-  if (k.D == 64) return launch_fwd_64_bf16_bf16(a, k, grid, st);
-  return launch_fwd_32_bf16_bf16(a, k, grid, st);
+  if (k.D == 128) return launch_fwd2_128(a, k, grid, st);
+  if (k.D == 64) return launch_fwd2_64(a, k, grid, st);
+  return launch_fwd2_32(a, k, grid, st);
 }
 
 #define JATTN_DISPATCH_BWD(KIND)                                              \

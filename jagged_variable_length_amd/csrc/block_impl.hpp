@@ -111,11 +111,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
   char* vt = kt + T::BYTES;
   // two waves share one worker (wave pair) and take alternate units of it
   const int worker = xcd_worker(blockIdx.x, gridDim.x) * 2 + (wave >> 1);
-  const int u_end = a.worker_off[worker + 1];
+  const int u_end = uniform(a.worker_off[worker + 1]);
   const int HD = a.H * D;
 
   for (int u = a.worker_off[worker] + (wave & 1); u < u_end; u += 2) {
-    const i32x4 unit = reinterpret_cast<const i32x4*>(a.units)[u];
+    const i32x4 unit = load_unit(a.units, u);
     const int b = unit[0], h = unit[1], t = unit[2];
     const Sample s = load_sample(a.samples, b);
     const int row0 = t * 64;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
     int r = 0;
     int64_t qbase = 0, kbase = 0;
     if (active) {
-      const i32x4 unit = reinterpret_cast<const i32x4*>(a.units)[u];
+      const i32x4 unit = load_unit(a.units, u);
       const int b = unit[0], h = unit[1], t = unit[2];
       const Sample s = load_sample(a.samples, b);
       const int row0 = t * 64;

@@ -43,11 +43,12 @@ __device__ __forceinline__ Sample load_sample(const int32_t* table, int b) {
   i32x4 a = p[0];
   i32x4 c = p[1];
   Sample s;
-  s.q0 = a[0];
-  s.lq = a[1];
-  s.k0 = a[2];
-  s.lk = a[3];
-  s.bias0 = (int64_t)(uint32_t)c[0] | ((int64_t)c[1] << 32);
+  s.q0 = __builtin_amdgcn_readfirstlane(a[0]);
+  s.lq = __builtin_amdgcn_readfirstlane(a[1]);
+  s.k0 = __builtin_amdgcn_readfirstlane(a[2]);
+  s.lk = __builtin_amdgcn_readfirstlane(a[3]);
+  s.bias0 = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane(c[0]) |
+            ((int64_t)__builtin_amdgcn_readfirstlane(c[1]) << 32);
   return s;
 }
 
@@ -66,10 +67,25 @@ __device__ __forceinline__ int xcd_worker(int block, int nblocks) {
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Every call site passes a per-unit (wave-uniform) base and size; reading
+// them through readfirstlane lets the descriptor live in SGPRs, as buffer
+// instructions require, instead of a per-lane loop over descriptors.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* q = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   // word 3 = 0x00020000: 32-bit data format for raw (untyped) access on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Unit record (b, h, tile, cost), read once per wave and kept in SGPRs.
+__device__ __forceinline__ i32x4 load_unit(const int32_t* units, int u) {
+  const i32x4 x = reinterpret_cast<const i32x4*>(units)[u];
+  return i32x4{uniform(x[0]), uniform(x[1]), uniform(x[2]), uniform(x[3])};
 }
 
 __device__ __forceinline__ i32x4 buf_load16(rsrc_t r, uint32_t voff) {

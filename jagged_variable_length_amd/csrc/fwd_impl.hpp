@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int wq = wave % WQ, wk = wave / WQ;
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_end = a.worker_off[worker + 1];
+  const int u_end = uniform(a.worker_off[worker + 1]);
   const int HD = a.H * D;
 
   // staging coordinates: this thread moves chunk column sc of rows sr0..sr0+CPT-1
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int bc = tid % BN;
   const int br0 = tid / BN;
 
-  for (int u = a.worker_off[worker]; u < u_end; ++u) {
-    const i32x4 unit = reinterpret_cast<const i32x4*>(a.units)[u];
+  for (int u = uniform(a.worker_off[worker]); u < u_end; ++u) {
+    const i32x4 unit = load_unit(a.units, u);
     const int b = unit[0], h = unit[1], qt = unit[2], ntiles = unit[3];
     const Sample s = load_sample(a.samples, b);
     const int qrow = qt * BM + wq * 32 + l32;  // this lane's query row in the sample
@@ -184,15 +184,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         vreg[j] = buf_load16(rv, voff);
       }
       if constexpr (BIAS) {
+        // rows qt*BM + br0 + i*(256/BN) of column t*BN + bc; a column past
+        // the sample end is pushed out of the buffer range (reads zero)
         const int kv = t * BN + bc;
+        const uint32_t step = (uint32_t)(kThreads / BN) * s.lk * SZ;
+        uint32_t voff = (uint32_t)((qt * BM + br0) * s.lk + kv) * SZ;
+        voff = (kv < s.lk) ? voff : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-          const int qr = qt * BM + br0 + i * (kThreads / BN);
-          const uint32_t voff = (kv < s.lk) ? (uint32_t)(qr * s.lk + kv) * SZ : 0x80000000u;
           if constexpr (SZ == 2)
-            breg[i] = buf_load2(rb, voff);
+            breg[i] = buf_load2(rb, voff + i * step);
           else
-            breg[i] = buf_load4(rb, voff);
+            breg[i] = buf_load4(rb, voff + i * step);
         }
       }
     };

@@ -107,6 +107,11 @@ JATTN_DECLARE_DI(64, f32)
 JATTN_DECLARE_DI(32, bf16)
 JATTN_DECLARE_DI(32, f32)
 
+// bf16 forward (LDS-DMA pipeline); one translation unit per head dim
+hipError_t launch_fwd2_128(const FwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_fwd2_64(const FwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_fwd2_32(const FwdArgs&, const KernelSel&, int, hipStream_t);
+
 hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_dq(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);

@@ -1,0 +1,117 @@
+// LDS tile helpers for gfx950: row-major bf16 tiles filled straight from HBM
+// with buffer loads whose destination is LDS, XOR-swizzled 16-byte chunks,
+// and transposed operand reads with ds_read_b64_tr_b16.
+#pragma once
+#include "common.hpp"
+
+namespace jattn {
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor as four SGPR words (base, size, raw 32-bit format) for
+// the LDS-destination loads below.  Inputs are wave-uniform at every call.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p), (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
+// HBM -> LDS loads (M0 = LDS base of the 64-lane group, lane l writes at
+// M0 + 16*l, or a 4-byte slot per lane for the 2-byte form).  Issued as
+// inline asm so that the compiler does not attach its own conservative
+// vmcnt waits to unrelated LDS reads; the kernels wait for these loads
+// explicitly (s_waitcnt vmcnt + barrier) before reading the data.
+__device__ __forceinline__ void lds_dma16(const i32x4& r, const char* lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const i32x4& r, const char* lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+               : "memory");
+}
+// 2-byte element into a zero-extended 4-byte slot (lane l -> slot l)
+__device__ __forceinline__ void lds_dma2(const i32x4& r, const char* lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+               : "memory");
+}
+
+// Row-major tile of bf16 rows of D elements with PAD spare 16-byte slots per
+// row (pitch = (D/8 + PAD) * 16 bytes).  The padding spreads consecutive rows
+// over the LDS banks, and since addresses are row * pitch + column, every
+// fragment of one lane is a fixed immediate offset from one base register.
+// Loads go straight from HBM into LDS: one instruction fills 64 consecutive
+// 16-byte slots, and lanes that land on a pad slot load out of range (zero).
+template <int D, int PAD>
+struct PadTile {
+  static constexpr int CPR = D / 8;      // 16-byte chunks of data per row
+  static constexpr int SPR = CPR + PAD;  // slots per row
+  static constexpr int PITCH = SPR * 16;
+  template <int ROWS>
+  static constexpr int ninst() { return (ROWS * SPR + 63) / 64; }
+  template <int ROWS>
+  static constexpr int bytes() { return ninst<ROWS>() * 1024; }
+  static __device__ __forceinline__ int off(int r, int col) { return r * PITCH + col * 2; }
+};
+
+// Rows [row0, row0 + ROWS) of one (sample, head) into a padded tile; the load
+// instructions are dealt round-robin over `nparts` waves.  Rows at or past the
+// resource end arrive as zeros.
+template <int D, int PAD, int ROWS>
+__device__ __forceinline__ void load_rows(char* tile, const i32x4& r, int row0, int HD, int lane, int part, int nparts) {
+  using T = PadTile<D, PAD>;
+  constexpr int NI = T::template ninst<ROWS>();
+  for (int inst = part; inst < NI; inst += nparts) {
+    const int slot = inst * 64 + lane;
+    const int rr = slot / T::SPR, ch = slot % T::SPR;
+    const uint32_t voff = (ch < T::CPR && rr < ROWS) ? (uint32_t)((row0 + rr) * HD + ch * 8) * 2 : 0x80000000u;
+    lds_dma16(r, tile + inst * 1024, voff);
+  }
+}
+
+// B/A fragment of a row operand: 8 bf16 of row `row`, columns kk*16 + g*8 ..
+template <int D, int PAD>
+__device__ __forceinline__ bf16x8 rows_frag(const char* tile, int row, int kk, int g) {
+  return *reinterpret_cast<const bf16x8*>(tile + PadTile<D, PAD>::off(row, kk * 16 + g * 8));
+}
+
+// A fragment of X^T for MFMA 32x32x16: lane l gets X[rows][col0 + l%32] for the
+// 8 rows that accumulator block `blk`, step `st` assigns to lane half g
+// (rows blk*32 + 16st + 4g + 0..3 and +8..+11).  Uses ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element i%4 of the 8-byte
+// pieces addressed by lanes i/4 + 4k, so lane j addresses row base + j/4,
+// columns col0 + 4*(j%4) .. +3.
+template <int D, int PAD>
+__device__ __forceinline__ bf16x8 trans_frag(const char* tile, int blk, int st, int col0, int lane) {
+  const int i = lane & 15, grp = (lane >> 4) & 1, g = lane >> 5;
+  const int col = col0 + 16 * grp + 4 * (i & 3);
+  const int r1 = blk * 32 + 16 * st + 4 * g + (i >> 2);
+  v4i16_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if __HIP_DEVICE_COMPILE__
+  lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + PadTile<D, PAD>::off(r1, col)));
+  hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + PadTile<D, PAD>::off(r1 + 8, col)));
+#endif
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 pack8v(const f32x16& v, int off) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)v[off + j];
+  return r;
+}
+
+}  // namespace jattn

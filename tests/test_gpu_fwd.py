@@ -71,13 +71,23 @@ def test_fwd_gdpa(act, split):
             assert np.all(np.abs(o[sq, h] - ro[sq, h]) <= bound), (b, h)
 
 
-def test_fwd_short_query_softmax_split_keys():
-    say("case: softmax with 32-row queries (key-split combine)")
+@pytest.mark.parametrize("D,bias", [(64, True), (128, False)])
+def test_fwd_short_query_softmax_split_keys(D, bias):
+    """32-row queries: the key tiles are split over the waves and combined."""
+    say(f"case: softmax with 32-row queries (key-split combine) D={D} bias={bias}")
     lq = [32, 20, 1, 32]
     lk = [700, 0, 129, 64]
-    inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=6, bias=True)
-    op, o, lse = _run_fwd(inp, bias=True)
+    inp = gen.make_custom(lq, lk, 2, D, "bf16", seed=6, bias=bias)
+    op, o, lse = _run_fwd(inp, bias=bias)
     assert op.info.fwd.tile_rows == 32
+    _compare(inp, op, o, lse)
+
+
+def test_fwd_short_query_bias_d128_uses_regular_shape():
+    say("case: 32-row queries with bias at D=128 (regular shape)")
+    inp = gen.make_custom([32, 20, 32], [700, 9, 64], 2, 128, "bf16", seed=7, bias=True)
+    op, o, lse = _run_fwd(inp, bias=True)
+    assert op.info.fwd.tile_rows == 128
     _compare(inp, op, o, lse)
 
 
