@@ -41,7 +41,22 @@ def parse():
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    """Plain device copy of a known size: the reference point that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the attention kernels to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
 def kernel_work(w, info, es_in, es_out, es_g, es_db=4):
@@ -137,6 +152,9 @@ def main():
               "(attention has no cross-GPU exchange; the sharding design is per-sample data parallel)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return
 
     import torch
     from jagged_variable_length_amd import attention as A

@@ -142,11 +142,16 @@ __device__ __forceinline__ constexpr int perm32(int r) {
   return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 
+// Combine lane l with lane l^32.  v_permlane32_swap with both operands = x
+// leaves {x of lane l%32, x of lane l%32 + 32} in every lane, so both halves
+// compute the same value in the same order.
 __device__ __forceinline__ float wave_xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_xor32_sum(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // erf-GELU and SiLU (GDPA activations) and their derivatives, fp32.

@@ -47,7 +47,9 @@ struct Fwd2Shape {
   static constexpr bool S_IN_STAGE = (WK > 1) && STAGE >= COMB_O + STATS;
   static constexpr int EXTRA = (WK > 1) ? ((O_IN_STAGE ? 0 : COMB_O) + (S_IN_STAGE ? 0 : STATS)) : 0;
   static constexpr int SMEM = 2 * STAGE + EXTRA;
+  static constexpr int BIAS_ROWS = BM * (BN / 64);  // 64-key bias row segments per step
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(!BIAS || (BIAS_ROWS % NW == 0 && NW % (BN / 64) == 0), "bias segments must deal evenly");
 };
 
 template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   constexpr float kLazy = 8.0f;  // rescale only when a row max grows by > 2^8
 
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int wq = wave % WQ, wk = wave / WQ;
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
@@ -69,10 +71,17 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   auto stage_k = [&](int s) { return smem + s * Sh::STAGE; };
   auto stage_v = [&](int s) { return smem + s * Sh::STAGE + Sh::K_BYTES; };
   auto stage_b = [&](int s) { return smem + s * Sh::STAGE + Sh::K_BYTES + Sh::V_BYTES; };
+  const uint32_t smem_lds = lds_addr(smem);
+
+  RowLoader<D, 1, BN, NW> kload;
+  RowLoader<D, 2, BN, NW> vload;
+  kload.init(wave, lane, HD);
+  vload.init(wave, lane, HD);
 
   struct UnitInfo {
     int b, h, qt, n;
     Sample s;
+    i32x4 rk, rv, rb;  // descriptors at row 0 of this (sample, head)
   };
   auto fetch = [&](int u) {
     UnitInfo x;
@@ -82,26 +91,39 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     x.qt = un[2];
     x.n = un[3];
     x.s = load_sample(a.samples, x.b);
+    const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D;
+    x.rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + kvo, 0);
+    x.rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + kvo, 0);
+    if constexpr (BIAS)
+      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk, 0);
     return x;
   };
-  auto kv_rsrc = [&](const void* base, const UnitInfo& x) {
-    return rsrc_words(reinterpret_cast<const bf16*>(base) + ((int64_t)x.s.k0 * a.H + x.h) * D,
-                      (uint32_t)x.s.lk * HD * 2);
-  };
-  // issue the HBM -> LDS loads of step t of unit x into stage st
+  // issue the HBM -> LDS loads of step t of unit x into stage st: the K and V
+  // descriptors start at the step's first key row and end at the sample end
   auto issue_step = [&](const UnitInfo& x, int t, int st) {
-    const i32x4 rk = kv_rsrc(a.k, x), rv = kv_rsrc(a.v, x);
-    load_rows<D, 1, BN>(stage_k(st), rk, t * BN, HD, lane, wave, NW);
-    load_rows<D, 2, BN>(stage_v(st), rv, t * BN, HD, lane, wave, NW);
+    const uint32_t sb = smem_lds + st * Sh::STAGE;
+    const int64_t row0 = (int64_t)t * BN;
+    const int64_t rec = (int64_t)(x.s.lk - t * BN) * HD * 2;
+    kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
+    vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
     if constexpr (BIAS) {
-      const bf16* bb = reinterpret_cast<const bf16*>(a.bias) + x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
-      const i32x4 rb = rsrc_words(bb, (uint32_t)x.s.lq * x.s.lk * 2);
-      char* bt = stage_b(st);
-      for (int i = wave; i < BM * (BN / 64); i += NW) {
-        const int r = i / (BN / 64), cc = i % (BN / 64);
-        const int col = t * BN + cc * 64 + lane;
-        const uint32_t voff = (col < x.s.lk) ? (uint32_t)((x.qt * BM + r) * x.s.lk + col) * 2 : 0x80000000u;
-        lds_dma2(rb, bt + r * Sh::BROW + cc * 256, voff);
+      // one 64-key segment of one query row per load, lane l -> key l; the
+      // descriptor covers exactly the valid part of the segment.  A wave
+      // keeps one segment column and walks down the rows.
+      constexpr int SEGS = BN / 64, RSTEP = NW / SEGS;
+      const int cc = wave % SEGS, c0 = t * BN + cc * 64;
+      const int nk = max(min(x.s.lk - c0, 64), 0) * 2;
+      int qr = x.qt * BM + wave / SEGS;
+      i32x4 rb = rsrc_at(x.rb, ((int64_t)qr * x.s.lk + c0) * 2, 0);
+      uint32_t m0 = sb + Sh::K_BYTES + Sh::V_BYTES + (wave / SEGS) * Sh::BROW + cc * 256;
+      const int64_t row_bytes = (int64_t)RSTEP * x.s.lk * 2;
+#pragma unroll
+      for (int j = 0; j < Sh::BIAS_ROWS / NW; ++j) {
+        rb[2] = qr < x.s.lq ? nk : 0;
+        lds_dma2(rb, m0, lane * 2);
+        rb = rsrc_at(rb, row_bytes, 0);
+        m0 += RSTEP * Sh::BROW;
+        qr += RSTEP;
       }
     }
   };
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     f32x16 oacc[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
+    float m_run = 0.0f, l_run = 0.0f, lr_run = 0.0f;
 
     for (int t = 0; t < n; ++t) {
       wait_vmcnt0();
@@ -163,32 +185,48 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           for (int j = 0; j < 4; ++j) p[a4 * 4 + j] = __uint_as_float(w[j] << 16);
         }
       }
+      bf16x8 pf[2], pl[2];
       if constexpr (SOFTMAX) {
+        // scores in log2 units relative to the running max: x - m
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float x = BIAS ? fmaf(p[i], kLog2e, sacc[i] * a.scale_log2) : sacc[i] * a.scale_log2;
-          p[i] = x;
-          mx = fmaxf(mx, x);
+          const float c = BIAS ? fmaf(p[i], kLog2e, -m_run) : -m_run;
+          p[i] = fmaf(sacc[i], a.scale_log2, c);
+          mx = fmaxf(mx, p[i]);
         }
         mx = wave_xor32_max(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = fast_exp2(m_run - m_new);
+        if (t == 0) {
+          // first step: the running max starts at this step's max (m_run was 0)
+          m_run = mx;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p[i] -= mx;
+        } else if (__builtin_amdgcn_ballot_w64(mx > kLazy) != 0) {
+          const float delta = fmaxf(mx, 0.0f);
+          const float alpha = fast_exp2(-delta);
           l_run *= alpha;
           lr_run *= alpha;
 #pragma unroll
           for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-          m_run = m_new;
+          m_run += delta;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p[i] -= delta;
         }
         float rs = 0.0f, rsr = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(p[i] - m_run);
-          const float er = (float)(bf16)e;  // P as the PV MFMA sees it
-          rs += e;
-          rsr += er;
-          p[i] = er;
+          p[i] = fast_exp2(p[i]);
+          rs += p[i];
+        }
+        // the PV MFMA sees P rounded to bf16; the output is normalised by the
+        // sum of exactly those values (v_dot2_f32_bf16 against ones)
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          pf[st] = pack8(&p[st * 8]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            rsr = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[st][2 * j], pf[st][2 * j + 1]}, ones, rsr, false);
         }
         l_run += rs;
         lr_run += rsr;
@@ -198,23 +236,27 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           const float x = BIAS ? p[i] + sacc[i] * a.scale : sacc[i] * a.scale;
           p[i] = act_fwd(ACT, x);
         }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          pf[st] = pack8(&p[st * 8]);
+          if constexpr (SPLIT) {
+            float r8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r8[j] = p[st * 8 + j] - (float)pf[st][j];
+            pl[st] = pack8(r8);
+          }
+        }
       }
 
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 pf = pack8(&p[st * 8]);
-        bf16x8 pl;
-        if constexpr (SPLIT) {
-          float r8[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) r8[j] = p[st * 8 + j] - (float)pf[j];
-          pl = pack8(r8);
-        }
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           const bf16x8 vf = trans_frag<D, 2>(vt, wk, st, d * 32, lane);
-          oacc[d] = Elem<bf16>::mma(vf, pf, oacc[d]);
-          if constexpr (SPLIT) oacc[d] = Elem<bf16>::mma(vf, pl, oacc[d]);
+          oacc[d] = Elem<bf16>::mma(vf, pf[st], oacc[d]);
+          // split operands matter for the activation path only: softmax
+          // already normalises by the sum of the rounded P
+          if constexpr (SPLIT && !SOFTMAX) oacc[d] = Elem<bf16>::mma(vf, pl[st], oacc[d]);
         }
       }
       stage ^= 1;
@@ -228,6 +270,13 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       const float pad_e = fast_exp2(-m_run);
       l_run = wave_xor32_sum(l_run) - (float)npad * pad_e;
       lr_run = wave_xor32_sum(lr_run) - (float)npad * (float)(bf16)pad_e;
+      if (cur.s.lk <= wk * 32) {
+        // this wave's key block lies wholly past the sample end: it holds no
+        // term of the row (its O is zero since those V rows read as zero)
+        m_run = -INFINITY;
+        l_run = 0.0f;
+        lr_run = 0.0f;
+      }
     }
     const int qrow = cur.qt * BM + wq * 32 + l32;
     TO* orow = reinterpret_cast<TO*>(a.o) + ((int64_t)(cur.s.q0 + qrow) * a.H + cur.h) * D;

@@ -18,26 +18,37 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
                (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+// LDS byte address of a pointer into a __shared__ array, as M0 and the ds_*
+// instructions see it.  Taken once per kernel; stage and tile addresses are
+// then plain 32-bit scalar offsets from it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
 
-// HBM -> LDS loads (M0 = LDS base of the 64-lane group, lane l writes at
-// M0 + 16*l, or a 4-byte slot per lane for the 2-byte form).  Issued as
-// inline asm so that the compiler does not attach its own conservative
-// vmcnt waits to unrelated LDS reads; the kernels wait for these loads
-// explicitly (s_waitcnt vmcnt + barrier) before reading the data.
-__device__ __forceinline__ void lds_dma16(const i32x4& r, const char* lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+// Descriptor moved `bytes_off` bytes forward with `records` bytes left
+// (records <= 0 -> every load of it reads zero).  Scalar arithmetic only.
+__device__ __forceinline__ i32x4 rsrc_at(const i32x4& r, int64_t bytes_off, int64_t records) {
+  const uint64_t p = ((uint64_t)(uint32_t)r[0] | ((uint64_t)(uint32_t)r[1] << 32)) + (uint64_t)bytes_off;
+  const int64_t n = records < 0 ? 0 : records;
+  return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)(uint32_t)n, r[3]};
+}
+
+// HBM -> LDS loads (M0 = LDS byte address of the 64-lane group; lane l writes
+// at M0 + 16*l, or the 4-byte slot M0 + 4*l for the dword and 2-byte forms,
+// the 2-byte value zero-extended).  Issued as inline asm so that the compiler
+// does not attach its own conservative vmcnt waits to unrelated LDS reads; the
+// kernels wait for these loads explicitly (s_waitcnt vmcnt + barrier) before
+// reading the data.
+__device__ __forceinline__ void lds_dma16(const i32x4& r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
-__device__ __forceinline__ void lds_dma4(const i32x4& r, const char* lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+__device__ __forceinline__ void lds_dma4(const i32x4& r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
-// 2-byte element into a zero-extended 4-byte slot (lane l -> slot l)
-__device__ __forceinline__ void lds_dma2(const i32x4& r, const char* lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(lds_addr(lds)), "v"(voff), "s"(r)
+__device__ __forceinline__ void lds_dma2(const i32x4& r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
 
@@ -45,8 +56,8 @@ __device__ __forceinline__ void lds_dma2(const i32x4& r, const char* lds, uint32
 // row (pitch = (D/8 + PAD) * 16 bytes).  The padding spreads consecutive rows
 // over the LDS banks, and since addresses are row * pitch + column, every
 // fragment of one lane is a fixed immediate offset from one base register.
-// Loads go straight from HBM into LDS: one instruction fills 64 consecutive
-// 16-byte slots, and lanes that land on a pad slot load out of range (zero).
+// One load instruction fills 64 consecutive 16-byte slots; lanes that land on
+// a pad slot load out of range (zero).
 template <int D, int PAD>
 struct PadTile {
   static constexpr int CPR = D / 8;      // 16-byte chunks of data per row
@@ -59,20 +70,34 @@ struct PadTile {
   static __device__ __forceinline__ int off(int r, int col) { return r * PITCH + col * 2; }
 };
 
-// Rows [row0, row0 + ROWS) of one (sample, head) into a padded tile; the load
-// instructions are dealt round-robin over `nparts` waves.  Rows at or past the
-// resource end arrive as zeros.
-template <int D, int PAD, int ROWS>
-__device__ __forceinline__ void load_rows(char* tile, const i32x4& r, int row0, int HD, int lane, int part, int nparts) {
+// Loads ROWS rows of one (sample, head) into a PadTile, the load instructions
+// dealt round-robin over NPARTS waves.  The per-lane source offsets depend
+// only on the row pitch in HBM (H*D elements), so they are computed once; a
+// step only moves the scalar descriptor (rsrc_at) to its first row, and rows
+// at or past the descriptor end arrive as zeros.
+template <int D, int PAD, int ROWS, int NPARTS>
+struct RowLoader {
   using T = PadTile<D, PAD>;
-  constexpr int NI = T::template ninst<ROWS>();
-  for (int inst = part; inst < NI; inst += nparts) {
-    const int slot = inst * 64 + lane;
-    const int rr = slot / T::SPR, ch = slot % T::SPR;
-    const uint32_t voff = (ch < T::CPR && rr < ROWS) ? (uint32_t)((row0 + rr) * HD + ch * 8) * 2 : 0x80000000u;
-    lds_dma16(r, tile + inst * 1024, voff);
+  static constexpr int NI = T::template ninst<ROWS>();
+  static constexpr int NJ = (NI + NPARTS - 1) / NPARTS;
+  uint32_t voff[NJ];
+  __device__ __forceinline__ void init(int part, int lane, int HD) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int slot = (part + j * NPARTS) * 64 + lane;
+      const int rr = slot / T::SPR, ch = slot % T::SPR;
+      voff[j] = (ch < T::CPR && rr < ROWS) ? (uint32_t)(rr * HD + ch * 8) * 2 : 0x80000000u;
+    }
   }
-}
+  // part must be wave-uniform; tile is the LDS byte address of the tile
+  __device__ __forceinline__ void issue(uint32_t tile, const i32x4& r, int part) const {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int inst = part + j * NPARTS;
+      if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, voff[j]);
+    }
+  }
+};
 
 // B/A fragment of a row operand: 8 bf16 of row `row`, columns kk*16 + g*8 ..
 template <int D, int PAD>
