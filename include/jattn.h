@@ -167,7 +167,8 @@ int jattn_bwd(const jattn_plan* plan, const void* q, const void* k, const void* 
               void* dk, void* dv, void* dbias, void* workspace, void* stream);
 
 /* Backward stages (bit mask for jattn_bwd_stages). */
-#define JATTN_BWD_PREP 1 /* Di = rowsum(dO * O) into the workspace (softmax, mask NONE) */
+#define JATTN_BWD_PREP 1 /* Di = rowsum(dO * O) and LSE * log2(e) into the workspace
+                            (softmax, mask NONE) */
 #define JATTN_BWD_DKDV 2 /* dK, dV (and dBias) */
 #define JATTN_BWD_DQ 4   /* dQ */
 #define JATTN_BWD_ALL 7

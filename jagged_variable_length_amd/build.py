@@ -36,6 +36,8 @@ def units():
     u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", [])]
     for d in (128, 64, 32):
         u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
+        for tg in ("bf16", "f32"):
+            u.append(("bwd2_inst.hip", f"dkdv2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
     for d, ti, to in FWD_INST:
         if ti == "f32":
             u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))

@@ -26,7 +26,7 @@ struct jattn_plan {
   std::vector<int32_t> image;  // uploaded plan (int32 words)
   int64_t off_samples = 0, off_fwd_u = 0, off_fwd_o = 0, off_dkdv_u = 0, off_dkdv_o = 0;
   int64_t off_dq_u = 0, off_dq_o = 0, off_blk_u = 0, off_blk_o = 0;  // in int32 words
-  int64_t plan_bytes = 0, di_off = 0, workspace_bytes = 0;
+  int64_t plan_bytes = 0, di_off = 0, lse2_off = 0, workspace_bytes = 0;
 };
 
 namespace {
@@ -149,6 +149,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
       return fail(JATTN_E_SHAPE, "one sample must span < 2^31 bytes");
     if (d.has_bias && a * c * es >= (int64_t(1) << 31))
       return fail(JATTN_E_SHAPE, "one sample's bias block per head must span < 2^31 bytes");
+    if (d.has_bias && d.want_dbias && a * c * elem_size(d.dbias_dtype) >= (int64_t(1) << 31))
+      return fail(JATTN_E_SHAPE, "one sample's dbias block per head must span < 2^31 bytes");
     if (d.mask == JATTN_MASK_BLOCKDIAG64 && a != c)
       return fail(JATTN_E_SHAPE, "block-diagonal mode needs lq == lk for every sample");
     lq[b] = (int32_t)a;
@@ -208,6 +210,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
+    // the bf16 dK/dV kernel has no room for a bias tile with 128-query steps at D = 128
+    if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias && p->dkdv_wkv == 1) p->dkdv_wkv = 2;
     const int dkdv_tile = 32 * p->dkdv_wkv, dkdv_step = 32 * (4 / p->dkdv_wkv);
     jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd);
     jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq);
@@ -219,7 +223,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   append(p->image, p->block, &p->off_blk_u, &p->off_blk_o);
   p->plan_bytes = (int64_t)p->image.size() * 4;
   p->di_off = align_up(p->plan_bytes, 256);
-  p->workspace_bytes = p->di_off + align_up(p->Tq * d.H * 4, 256);
+  p->lse2_off = p->di_off + align_up(p->Tq * d.H * 4, 256);
+  p->workspace_bytes = p->lse2_off + align_up(p->Tq * d.H * 4, 256);
   *out = p;
   return ok();
 }
@@ -356,6 +361,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   float* di = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->di_off);
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lse2_off);
   KernelSel sel = base_sel(p);
   sel.out_f32 = p->desc.grad_dtype == JATTN_F32;
   sel.wq = p->dq_wq;
@@ -382,7 +388,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
     return ok();
   }
   if (softmax_dense && p->Tq > 0 && (stages & JATTN_BWD_PREP)) {
-    jattn::DiArgs da{o, dout, di, p->Tq * p->H};
+    jattn::DiArgs da{o, dout, di, p->Tq * p->H, lse, lse2};
     e = jattn::launch_di(da, sel, p->desc.out_dtype == JATTN_F32, st);
     if (e != hipSuccess) return hip_fail(e, "Di launch");
   }
@@ -394,6 +400,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   a.dout = dout;
   a.lse = lse;
   a.di = di;
+  a.lse2 = lse2;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -450,7 +457,22 @@ hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_
   }
 
 JATTN_DISPATCH_BWD(dq)
-JATTN_DISPATCH_BWD(dkdv)
+#undef JATTN_DISPATCH_BWD
+
+hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.in_f32) {
+    if (k.D == 64) return launch_dkdv_64_f32_f32(a, k, grid, st);
+    return launch_dkdv_32_f32_f32(a, k, grid, st);
+  }
+  if (k.out_f32) {
+    if (k.D == 128) return launch_dkdv2_128_f32(a, k, grid, st);
+    if (k.D == 64) return launch_dkdv2_64_f32(a, k, grid, st);
+    return launch_dkdv2_32_f32(a, k, grid, st);
+  }
+  if (k.D == 128) return launch_dkdv2_128_bf16(a, k, grid, st);
+  if (k.D == 64) return launch_dkdv2_64_bf16(a, k, grid, st);
+  return launch_dkdv2_32_bf16(a, k, grid, st);
+}
 
 hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_t st) {
   if (k.in_f32) {

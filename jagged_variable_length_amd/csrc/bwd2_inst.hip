@@ -1,0 +1,58 @@
+// bf16 dK/dV kernel instances for one head dim and gradient type; compiled
+// with -DJ_D=<32|64|128> -DJ_TG=<bf16|f32>.
+#include "bwd2_impl.hpp"
+
+#if !defined(J_D) || !defined(J_TG)
+#error "J_D and J_TG must be defined"
+#endif
+
+namespace jattn {
+
+typedef float f32;
+
+namespace {
+
+template <int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT>
+hipError_t dkdv2_one(const BwdArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dkdv2_kernel<J_TG, D, WKV, WKQ, ACT, BIAS, DBIAS, SPLIT>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int WKV, int WKQ, int ACT, bool SPLIT>
+hipError_t dkdv2_bias(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if constexpr (D == 128 && WKQ == 4) {
+    // 128 queries per step leave no room for a bias tile at this head dim
+    if (k.bias) return hipErrorInvalidValue;
+  } else if (k.bias) {
+    if (k.dbias && k.dbias_f32) return dkdv2_one<D, WKV, WKQ, ACT, true, 2, SPLIT>(a, grid, st);
+    if (k.dbias) return dkdv2_one<D, WKV, WKQ, ACT, true, 1, SPLIT>(a, grid, st);
+    return dkdv2_one<D, WKV, WKQ, ACT, true, 0, SPLIT>(a, grid, st);
+  }
+  return dkdv2_one<D, WKV, WKQ, ACT, false, 0, SPLIT>(a, grid, st);
+}
+
+template <int D, int WKV, int WKQ, int ACT>
+hipError_t dkdv2_act(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.split) return dkdv2_bias<D, WKV, WKQ, ACT, true>(a, k, grid, st);
+  return dkdv2_bias<D, WKV, WKQ, ACT, false>(a, k, grid, st);
+}
+
+template <int D, int WKV, int WKQ>
+hipError_t dkdv2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.act == kSoftmax) return dkdv2_act<D, WKV, WKQ, kSoftmax>(a, k, grid, st);
+  if (k.act == kGelu) return dkdv2_act<D, WKV, WKQ, kGelu>(a, k, grid, st);
+  return dkdv2_act<D, WKV, WKQ, kSilu>(a, k, grid, st);
+}
+
+}  // namespace
+
+#define JATTN_DKDV2_NAME_(D, TG) launch_dkdv2_##D##_##TG
+#define JATTN_DKDV2_NAME(D, TG) JATTN_DKDV2_NAME_(D, TG)
+
+hipError_t JATTN_DKDV2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.wkv == 4) return dkdv2_shape<J_D, 4, 1>(a, k, grid, st);
+  if (k.wkv == 2) return dkdv2_shape<J_D, 2, 2>(a, k, grid, st);
+  return dkdv2_shape<J_D, 1, 4>(a, k, grid, st);
+}
+
+}  // namespace jattn

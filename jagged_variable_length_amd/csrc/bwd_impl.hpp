@@ -46,7 +46,10 @@ __global__ __launch_bounds__(kThreads) void di_kernel(DiArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < a.rows && (tid % LPR) == 0) a.di[row] = acc;
+  if (row < a.rows && (tid % LPR) == 0) {
+    a.di[row] = acc;
+    if (a.lse2 != nullptr) a.lse2[row] = a.lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -32,7 +32,9 @@ struct DiArgs {
   const void* o;
   const void* dout;
   float* di;
-  int64_t rows;  // Tq * H
+  int64_t rows;       // Tq * H
+  const float* lse;   // [Tq, H] natural log (may be null)
+  float* lse2;        // out: lse * log2(e), read by the bf16 backward kernels
 };
 
 struct BwdArgs {
@@ -43,6 +45,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;  // [Tq, H] natural log
   const float* di;   // [Tq, H]
+  const float* lse2; // [Tq, H] lse * log2(e)
   void* dq;
   void* dk;
   void* dv;
@@ -106,6 +109,14 @@ JATTN_DECLARE_DI(64, bf16)
 JATTN_DECLARE_DI(64, f32)
 JATTN_DECLARE_DI(32, bf16)
 JATTN_DECLARE_DI(32, f32)
+
+// bf16 dK/dV (LDS-DMA pipeline); one translation unit per (head dim, gradient type)
+hipError_t launch_dkdv2_128_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dkdv2_128_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dkdv2_64_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dkdv2_64_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dkdv2_32_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dkdv2_32_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
 
 // bf16 forward (LDS-DMA pipeline); one translation unit per head dim
 hipError_t launch_fwd2_128(const FwdArgs&, const KernelSel&, int, hipStream_t);
