@@ -38,6 +38,7 @@ def units():
         u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
         for tg in ("bf16", "f32"):
             u.append(("bwd2_inst.hip", f"dkdv2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
+            u.append(("dq2_inst.hip", f"dq2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
     for d, ti, to in FWD_INST:
         if ti == "f32":
             u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))

@@ -206,6 +206,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     // the bf16 short-query forward has no room for a bias tile at D = 128
     if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias) p->fwd_wq = 4;
     p->dq_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
+    // nor has the bf16 short-query dQ kernel
+    if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias) p->dq_wq = 4;
     const int fwd_tile = 32 * p->fwd_wq, fwd_step = p->fwd_wq == 4 ? 64 : 128;
     const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
@@ -440,24 +442,20 @@ hipError_t launch_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_
   return launch_fwd2_32(a, k, grid, st);
 }
 
-#define JATTN_DISPATCH_BWD(KIND)                                              \
-  hipError_t launch_##KIND(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) { \
-    if (k.in_f32) {                                                              \
-      if (k.D == 64) return launch_##KIND##_64_f32_f32(a, k, grid, st);          \
-      return launch_##KIND##_32_f32_f32(a, k, grid, st);                         \
-    }                                                                            \
-    if (k.out_f32) {                                                             \
-      if (k.D == 128) return launch_##KIND##_128_bf16_f32(a, k, grid, st);       \
-      if (k.D == 64) return launch_##KIND##_64_bf16_f32(a, k, grid, st);         \
-      return launch_##KIND##_32_bf16_f32(a, k, grid, st);                        \
-    }                                                                            \
-    if (k.D == 128) return launch_##KIND##_128_bf16_bf16(a, k, grid, st);        \
-    if (k.D == 64) return launch_##KIND##_64_bf16_bf16(a, k, grid, st);          \
-    return launch_##KIND##_32_bf16_bf16(a, k, grid, st);                         \
+hipError_t launch_dq(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.in_f32) {
+    if (k.D == 64) return launch_dq_64_f32_f32(a, k, grid, st);
+    return launch_dq_32_f32_f32(a, k, grid, st);
   }
-
-JATTN_DISPATCH_BWD(dq)
-#undef JATTN_DISPATCH_BWD
+  if (k.out_f32) {
+    if (k.D == 128) return launch_dq2_128_f32(a, k, grid, st);
+    if (k.D == 64) return launch_dq2_64_f32(a, k, grid, st);
+    return launch_dq2_32_f32(a, k, grid, st);
+  }
+  if (k.D == 128) return launch_dq2_128_bf16(a, k, grid, st);
+  if (k.D == 64) return launch_dq2_64_bf16(a, k, grid, st);
+  return launch_dq2_32_bf16(a, k, grid, st);
+}
 
 hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.in_f32) {

@@ -1,0 +1,51 @@
+// bf16 dQ kernel instances for one head dim and gradient type; compiled with
+// -DJ_D=<32|64|128> -DJ_TG=<bf16|f32>.
+#include "dq2_impl.hpp"
+
+#if !defined(J_D) || !defined(J_TG)
+#error "J_D and J_TG must be defined"
+#endif
+
+namespace jattn {
+
+typedef float f32;
+
+namespace {
+
+template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
+hipError_t dq2_one(const BwdArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dq2_kernel<J_TG, J_D, WQ, WK, ACT, BIAS, SPLIT>), dim3(grid), dim3(64 * WQ * WK), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WQ, int WK, int ACT>
+hipError_t dq2_act(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if constexpr (J_D == 128 && WQ == 1) {
+    // a 128-key step leaves no room for a bias tile at this head dim
+    if (k.bias) return hipErrorInvalidValue;
+  } else if (k.bias) {
+    if (k.split) return dq2_one<WQ, WK, ACT, true, true>(a, grid, st);
+    return dq2_one<WQ, WK, ACT, true, false>(a, grid, st);
+  }
+  if (k.split) return dq2_one<WQ, WK, ACT, false, true>(a, grid, st);
+  return dq2_one<WQ, WK, ACT, false, false>(a, grid, st);
+}
+
+template <int WQ, int WK>
+hipError_t dq2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.act == kSoftmax) return dq2_act<WQ, WK, kSoftmax>(a, k, grid, st);
+  if (k.act == kGelu) return dq2_act<WQ, WK, kGelu>(a, k, grid, st);
+  return dq2_act<WQ, WK, kSilu>(a, k, grid, st);
+}
+
+}  // namespace
+
+#define JATTN_DQ2_NAME_(D, TG) launch_dq2_##D##_##TG
+#define JATTN_DQ2_NAME(D, TG) JATTN_DQ2_NAME_(D, TG)
+
+hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.wq == 4) return dq2_shape<4, 2>(a, k, grid, st);
+  return dq2_shape<1, 4>(a, k, grid, st);
+}
+
+}  // namespace jattn

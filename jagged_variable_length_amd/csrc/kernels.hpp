@@ -118,6 +118,14 @@ hipError_t launch_dkdv2_64_f32(const BwdArgs&, const KernelSel&, int, hipStream_
 hipError_t launch_dkdv2_32_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
 hipError_t launch_dkdv2_32_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
 
+// bf16 dQ (LDS-DMA pipeline); one translation unit per (head dim, gradient type)
+hipError_t launch_dq2_128_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dq2_128_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dq2_64_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dq2_64_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dq2_32_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
+hipError_t launch_dq2_32_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
+
 // bf16 forward (LDS-DMA pipeline); one translation unit per head dim
 hipError_t launch_fwd2_128(const FwdArgs&, const KernelSel&, int, hipStream_t);
 hipError_t launch_fwd2_64(const FwdArgs&, const KernelSel&, int, hipStream_t);

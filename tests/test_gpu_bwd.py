@@ -84,13 +84,17 @@ def test_bwd_gdpa_bias_long_queries(act):
     _compare(inp, op, got)
 
 
-def test_bwd_short_query_softmax():
-    say("case: bwd softmax 32-row queries (dQ key-split)")
+@pytest.mark.parametrize("D,bias,tile", [(64, True, 32), (128, False, 32), (128, True, 128)])
+def test_bwd_short_query_softmax(D, bias, tile):
+    """Short query tiles: the dQ kernel splits each 32-row group's keys over
+    4 waves; at D = 128 a bias tile does not fit that shape and the plan keeps
+    128-row query tiles."""
+    say(f"case: bwd softmax 32-row queries (dQ key-split) D={D} bias={bias}")
     lq = [32, 20, 1, 32]
     lk = [700, 0, 129, 64]
-    inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=6, bias=True)
-    op, got, _ = _run(inp, bias=True, want_dbias=True, grad_dtype="f32")
-    assert op.info.dq.tile_rows == 32
+    inp = gen.make_custom(lq, lk, 2, D, "bf16", seed=6, bias=bias)
+    op, got, _ = _run(inp, bias=bias, want_dbias=bias, grad_dtype="f32")
+    assert op.info.dq.tile_rows == tile
     _compare(inp, op, got)
 
 
