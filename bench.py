@@ -40,9 +40,13 @@ def parse():
     ap.add_argument("--order", default="heavy_first")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-mib", type=int, default=1024, help="copy size of the counter calibration")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CALIB_FETCH", "CALIB_WRITE"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE of this workload; "
+                         "the same two of --copy-calib) into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
@@ -94,20 +98,90 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
+KERNEL_KEYS = [("block_fwd_kernel", "block_fwd"), ("block_bwd_kernel", "block_bwd"), ("dkdv", "dkdv"),
+               ("dq2_kernel", "dq"), ("dq_kernel", "dq"), ("fwd2_kernel", "fwd"), ("fwd_kernel", "fwd"),
+               ("di_kernel", "prep")]
+
+
+def kernel_key(name):
+    """Launch name used in the bench line for a (mangled) kernel name."""
+    for pat, key in KERNEL_KEYS:
+        if pat in name:
+            return key
+    return None
+
+
+def traffic_for(kernel, cfg):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources and this workload (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
-    except Exception:
+    except (OSError, ValueError):
         return None
-    ent = d.get(kernel)
-    if not ent or ent.get("source_hash") != source_hash():
+    if d.get("source_hash") != source_hash():
         return None
-    return ent.get("bytes_per_launch")
+    ent = d.get("workloads", {}).get(str(cfg), {}).get(kernel)
+    return ent.get("bytes_per_launch") if ent else None
+
+
+def _pmc_means(folder, counter):
+    """Mean value of `counter` per dispatch, by kernel name, from the
+    *counter_collection.csv files rocprofv3 wrote under `folder`."""
+    import csv
+    per = {}
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if not f.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, f)) as fh:
+                for row in csv.DictReader(fh):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    key = (row["Kernel_Name"], row.get("Dispatch_Id", ""))
+                    per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {n: (float(np.mean(v)), len(v)) for n, v in out.items()}
+
+
+def traffic_summary(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each attention kernel,
+    scaled by what the same counters read for a plain copy of known size."""
+    fetch, write, cfetch, cwrite = args.traffic_summary
+    calib_bytes = args.calib_mib * (1 << 20)
+    cf_ = max(_pmc_means(cfetch, "FETCH_SIZE").items(), key=lambda kv: kv[1][1])
+    cw_ = max(_pmc_means(cwrite, "WRITE_SIZE").items(), key=lambda kv: kv[1][1])
+    f_read = calib_bytes / (cf_[1][0] * 1024.0)
+    f_write = calib_bytes / (cw_[1][0] * 1024.0)
+    res = {}
+    fm, wm = _pmc_means(fetch, "FETCH_SIZE"), _pmc_means(write, "WRITE_SIZE")
+    for name, (kib, n) in fm.items():
+        key = kernel_key(name)
+        if key is None:
+            continue
+        wkib = wm.get(name, (0.0, 0))[0]
+        rd, wr = kib * 1024.0 * f_read, wkib * 1024.0 * f_write
+        res[key] = {"kernel": name, "dispatches": n, "fetch_kib": kib, "write_kib": wkib,
+                    "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr}
+    out = {"source_hash": source_hash(), "calibration": {
+        "copy_bytes": calib_bytes, "copy_kernel": cf_[0], "fetch_kib": cf_[1][0], "write_kib": cw_[1][0],
+        "read_factor": f_read, "write_factor": f_write}, "workloads": {str(args.config): res}}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(p):
+        try:
+            old = json.load(open(p))
+        except (OSError, ValueError):
+            old = {}
+        if old.get("source_hash") == out["source_hash"]:
+            old.get("workloads", {}).update(out["workloads"])
+            out["workloads"] = old["workloads"]
+    with open(p, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -154,6 +228,9 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calibration(args.copy_calib, args.steps)
+        return
+    if args.traffic_summary:
+        traffic_summary(args)
         return
 
     import torch
@@ -240,7 +317,7 @@ def main():
     else:
         achieved = nflops / t / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
-    roof["traffic"] = traffic_for(dom)
+    roof["traffic"] = traffic_for(dom, cfg)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = nflops
