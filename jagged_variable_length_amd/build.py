@@ -10,6 +10,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -51,18 +52,40 @@ def _deps():
     return [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "jattn.h")]
 
 
+def _scratch_kernels(text):
+    """Kernels whose resource-usage remark reports scratch (private) memory.
+    Scratch accesses are vector memory operations: their waits would also
+    wait on the kernels' in-flight LDS prefetches, so none may use it."""
+    bad, name = [], None
+    for line in text.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src, name, defs, incremental):
     out = os.path.join(OBJ, name + ".o")
     if incremental and os.path.exists(out):
         newest = max(os.path.getmtime(p) for p in _deps())
         if os.path.getmtime(out) >= newest:
             return out, None
-    xflags = ["-x", "hip"] if src.endswith(".hip") else []
+    hip = src.endswith(".hip")
+    xflags = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if hip else []
     cmd = [HIPCC] + FLAGS + defs + xflags + ["-c", os.path.join(CSRC, src), "-o", out]
     p = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in (p.stdout + p.stderr).splitlines() if "packed-fp32-ops" not in l)
+    text = p.stdout + p.stderr
+    errs = "\n".join(l for l in text.splitlines()
+                     if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if p.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{errs}")
+    bad = _scratch_kernels(text)
+    if bad:
+        os.remove(out)
+        raise RuntimeError(f"{src} {' '.join(defs)}: kernels use scratch memory: {', '.join(bad)}")
     return out, errs.strip() or None
 
 

@@ -147,10 +147,10 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
       return fail(JATTN_E_OFFSETS, "total rows must be < 2^31");
     if (a * row_bytes >= (int64_t(1) << 31) || c * row_bytes >= (int64_t(1) << 31))
       return fail(JATTN_E_SHAPE, "one sample must span < 2^31 bytes");
-    if (d.has_bias && a * c * es >= (int64_t(1) << 31))
-      return fail(JATTN_E_SHAPE, "one sample's bias block per head must span < 2^31 bytes");
-    if (d.has_bias && d.want_dbias && a * c * elem_size(d.dbias_dtype) >= (int64_t(1) << 31))
-      return fail(JATTN_E_SHAPE, "one sample's dbias block per head must span < 2^31 bytes");
+    if (d.has_bias && a * c * es >= (int64_t(1) << 30))
+      return fail(JATTN_E_SHAPE, "one sample's bias block per head must span < 2^30 bytes");
+    if (d.has_bias && d.want_dbias && a * c * elem_size(d.dbias_dtype) >= (int64_t(1) << 30))
+      return fail(JATTN_E_SHAPE, "one sample's dbias block per head must span < 2^30 bytes");
     if (d.mask == JATTN_MASK_BLOCKDIAG64 && a != c)
       return fail(JATTN_E_SHAPE, "block-diagonal mode needs lq == lk for every sample");
     lq[b] = (int32_t)a;
@@ -316,6 +316,7 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   a.H = p->H;
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.4426950408889634f;
+  a.bias_elems = p->bias_elems;
   KernelSel sel = base_sel(p);
   sel.out_f32 = p->desc.out_dtype == JATTN_F32;
   sel.wq = p->fwd_wq;
@@ -411,6 +412,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   a.H = p->H;
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.4426950408889634f;
+  a.bias_elems = p->bias_elems;
   if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
     a.units = ws_ptr(workspace, p->off_dkdv_u);
     a.worker_off = ws_ptr(workspace, p->off_dkdv_o);

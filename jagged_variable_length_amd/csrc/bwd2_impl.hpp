@@ -77,10 +77,10 @@ struct Dkdv2Shape {
   static constexpr int PAD = 2;
   using QT = PadTile<D, PAD>;  // Q and dO rows: pitch = 32 (mod 256) bytes
   static constexpr int Q_BYTES = QT::template bytes<QS>();
-  static constexpr int SEGW = KT >= 64 ? 64 : 32;  // keys per bias load
-  static constexpr int SEGS = KT / SEGW;           // bias loads per query row
-  static constexpr int BROW = KT * 4 + 32;         // bias row: KT 4-byte slots, halves 32 banks apart
-  static constexpr int B_BYTES = BIAS ? QS * BROW : 0;
+  // bias rows (QS queries x KT keys, bf16): pitch = 16 (mod 64) dwords, so
+  // the two lane halves (query rows 4 apart) read disjoint banks
+  using BT = PadTile<KT, 1>;
+  static constexpr int B_BYTES = BIAS ? BT::template bytes<QS>() : 0;
   static constexpr int NRS = SOFTMAX ? 2 * ((QS + 63) / 64) : 0;  // row-stat loads (LSE*log2e, Di)
   static constexpr int RS_BYTES = NRS * 256;
   static constexpr int OFF_O = Q_BYTES;
@@ -95,10 +95,10 @@ struct Dkdv2Shape {
   static constexpr int SMEM = NS * STAGE;
   // loads that every wave issues per step (the minimum over waves)
   static constexpr int QNI = QT::template ninst<QS>();
-  static constexpr int L_MIN = 2 * (QNI / NW) + (BIAS ? QS * SEGS / NW : 0) + (NRS >= NW ? NRS / NW : 0);
+  static constexpr int L_MIN =
+      2 * (QNI / NW) + (BIAS ? BT::template ninst<QS>() / NW : 0) + (NRS >= NW ? NRS / NW : 0);
   static_assert(NS_FIT >= 2 && COMB <= STAGE, "LDS budget");
   static_assert(NW == 4, "four waves");
-  static_assert(!BIAS || (QS * SEGS) % NW == 0, "bias loads deal evenly");
   static_assert(L_MIN < 64, "vmcnt range");
 };
 
@@ -122,6 +122,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int H = a.H, HD = a.H * D;
 
   RowLoader<D, PAD, QS, NW> qload;
+  BiasLoader<KT, 1, QS, NW> bload;
   qload.init(wave, lane, HD);
   const uint32_t rs_voff = (uint32_t)lane * H * 4;  // row-stat load: lane l -> query row l of the load
 
@@ -129,9 +130,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     int h, kt, n;
     Sample s;
     i32x4 rq, rdo, rl, rd, rb;  // descriptors at query row 0 of the (sample, head)
+    int64_t brec;               // bytes from the bias block start to the end of the bias tensor
+    bool tail;                  // the bias block holds the tensor's last element
   };
   auto fetch = [&](int u) {
-    Unit x;
+    Unit x{};
     const i32x4 un = sload4(a.units, u);
     x.h = un[1];
     x.kt = un[2];
@@ -144,8 +147,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       x.rl = rsrc_words(a.lse2 + (int64_t)x.s.q0 * H + x.h, 0);
       x.rd = rsrc_words(a.di + (int64_t)x.s.q0 * H + x.h, 0);
     }
-    if constexpr (BIAS)
-      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk, 0);
+    if constexpr (BIAS) {
+      const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
+      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
+      x.brec = (a.bias_elems - e0) * 2;
+      x.tail = e0 + (int64_t)x.s.lq * x.s.lk == a.bias_elems;
+    }
     return x;
   };
 
@@ -172,24 +179,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       }
     }
     if constexpr (BIAS) {
-      // one segment of SEGW keys of one query row per load (lane l -> key l);
-      // the descriptor covers exactly the valid part of the segment
-      constexpr int RSTEP = NW / Sh::SEGS;
-      const int cc = wave % Sh::SEGS;
-      const int c0 = x.kt * KT + cc * Sh::SEGW;
-      const int nk = max(min(x.s.lk - c0, Sh::SEGW), 0) * 2;
-      int q = r0 + wave / Sh::SEGS;
-      i32x4 rb = rsrc_at(x.rb, ((int64_t)q * x.s.lk + c0) * 2, 0);
-      uint32_t m0 = sb + Sh::OFF_B + (wave / Sh::SEGS) * Sh::BROW + cc * 256;
-      const int64_t row_bytes = (int64_t)RSTEP * x.s.lk * 2;
-#pragma unroll
-      for (int j = 0; j < QS * Sh::SEGS / NW; ++j) {
-        rb[2] = q < x.s.lq ? nk : 0;
-        if (Sh::SEGW == 64 || lane < 32) lds_dma2(rb, m0, lane * 2);
-        rb = rsrc_at(rb, row_bytes, 0);
-        m0 += RSTEP * Sh::BROW;
-        q += RSTEP;
-      }
+      // query rows t*QS .., keys kt*KT .. of the bias block; the offsets follow lk
+      if (t == 0) bload.init(wave, lane, x.s.lk);
+      const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
+      bload.issue(sb + Sh::OFF_B, rsrc_at(x.rb, off, x.brec - off), wave);
     }
   };
 
@@ -301,12 +294,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     after_sdp();  // K/V fragments are dead from here on in the last step of a unit
     float p[16], ds[16];
+    const bool last_step = t + 1 == x.n;
     if constexpr (BIAS) {
-      // bias[q][key] for the 16 query rows of this lane (4-byte slots, bf16 in the low half)
-      const char* bt = qt + Sh::OFF_B + (wq * 32 + g * 4) * Sh::BROW + (wv * 32 + l32) * 4;
+      // bias[q][key] for the 16 query rows of this lane (keys past lk carry
+      // the next row's values; only their own, unstored columns see them)
+      const char* bt = qt + Sh::OFF_B + (wq * 32 + g * 4) * Sh::BT::PITCH + (wv * 32 + l32) * 2;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        p[i] = __uint_as_float(*reinterpret_cast<const uint32_t*>(bt + ((i >> 2) * 8 + (i & 3)) * Sh::BROW) << 16);
+        p[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(bt + acc_row(i, 0) * Sh::BT::PITCH) << 16);
+      if (last_step && x.tail) {
+        // the tensor's last element may straddle the end of the bias range by
+        // half a dword, which the range check drops: reload it
+        const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(a.bias) + (a.bias_elems - 1), 2);
+        const float last = __uint_as_float((uint32_t)buf_load2(rl, 0) << 16);
+        const int key = x.kt * KT + wv * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          p[i] = (key == x.s.lk - 1 && t * QS + wq * 32 + acc_row(i, g) == x.s.lq - 1) ? last : p[i];
+      }
     }
     if constexpr (SOFTMAX) {
       const char* rs = qt + Sh::OFF_RS;
@@ -331,6 +336,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const float xv = BIAS ? fmaf(sacc[i], a.scale, p[i]) : sacc[i] * a.scale;
         p[i] = act_fwd(ACT, xv);
         ds[i] = act_grad(ACT, xv) * dpacc[i];
+      }
+    }
+    if (last_step) {
+      // query rows past the sample end: zero Q, dO and row statistics make
+      // their terms vanish unless the bias of another row overflowed P
+      const int qrem = x.s.lq - (t * QS + wq * 32);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = acc_row(i, g) < qrem;
+        p[i] = ok ? p[i] : 0.0f;
+        ds[i] = ok ? ds[i] : 0.0f;
       }
     }
     if constexpr (DBIAS != 0) {
@@ -379,14 +395,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
   };
 
-  // wait for the loads of the step about to be computed: `recent` of the last
-  // NS-2 iterations issued a step's loads after it, and those may stay in flight
-  auto wait_step = [&](int recent) {
+  // Wait for the loads of the step about to be computed (and, at a unit
+  // boundary, the K/V loads issued in the previous step).  Vector memory
+  // operations complete in issue order, so every operation issued after the
+  // needed ones may stay in flight: the previous step's prefetch (`recent`)
+  // and the dBias stores of the last two steps (S per step, issued after
+  // each step's prefetch; the older batch only when no K/V load sits between).
+  auto wait_step = [&](bool boundary, int computed, int recent) {
     if constexpr (NS == 3) {
-      if (recent > 0)
-        wait_vmcnt<L>();
-      else
-        wait_vmcnt<0>();
+      constexpr int S = DBIAS != 0 ? 16 : 0;
+      static_assert(2 * S + L < 64, "vmcnt range");
+      const int ns = (computed >= 1 ? 1 : 0) + ((computed >= 2 && !boundary) ? 1 : 0);
+      if (recent > 0) {
+        if (ns == 2) wait_vmcnt<2 * S + L>();
+        else if (ns == 1) wait_vmcnt<S + L>();
+        else wait_vmcnt<L>();
+      } else {
+        if (ns == 2) wait_vmcnt<2 * S>();
+        else if (ns == 1) wait_vmcnt<S>();
+        else wait_vmcnt<0>();
+      }
     } else {
       wait_vmcnt<0>();
     }
@@ -395,8 +423,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // ---- consumer ----
   if (u_begin >= u_end) return;
   bf16x8 kf[NKK], vf[NKK];
-  int cs = 0;      // stage of the next step to compute
-  int recent = 0;  // did the previous iteration issue a step (NS == 3)
+  int cs = 0;        // stage of the next step to compute
+  int recent = 0;    // did the previous iteration issue a step (NS == 3)
+  int computed = 0;  // steps computed so far
   {
     int u0 = u_begin;
     Unit x0 = fetch(u0);
@@ -430,7 +459,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         ++un;
       }
       for (int t = 0; t < x.n; ++t) {
-        wait_step(recent);
+        wait_step(t == 0 && computed > 0, computed, recent);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
@@ -440,6 +469,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           recent = produce() ? 1 : 0;
         });
         cs = cs + 1 == NS ? 0 : cs + 1;
+        ++computed;
       }
     }
     store_unit(x, dkacc, dvacc, cs == 0 ? NS - 1 : cs - 1);

@@ -15,7 +15,10 @@
 //     dQ^T += K^T dS^T A = K^T via ds_read_b64_tr_b16, B = dS^T in-register
 // K, V and the bias tile travel HBM -> LDS with buffer loads whose
 // destination is LDS, double-buffered across steps and units; the key-split
-// partials of dQ are summed through LDS at the end of a unit.
+// partials of dQ are summed through LDS at the end of a unit.  K and V rows
+// are stored permuted within each 32-key block (RowLoader PERM), so that the
+// 16 scores of a lane are 16 consecutive keys and its bias values are two
+// aligned 16-byte LDS reads.
 #pragma once
 #include "common.hpp"
 #include "fwd_impl.hpp"
@@ -35,16 +38,20 @@ struct Dq2Shape {
   using VT = PadTile<D, 1>;  // V rows
   static constexpr int K_BYTES = KT::template bytes<BN>();
   static constexpr int V_BYTES = VT::template bytes<BN>();
-  static constexpr int BROW = BN * 4 + 16;  // bias row: BN 4-byte slots + pad
-  static constexpr int B_BYTES = BIAS ? BM * BROW : 0;
+  using BT = PadTile<BN, 1>;  // bias rows: pitch = 16 (mod 256) bytes, 16-byte reads conflict-free
+  static constexpr int B_BYTES = BIAS ? BT::template bytes<BM>() : 0;
   static constexpr int STAGE = K_BYTES + V_BYTES + B_BYTES;
-  // dQ^T partials of key blocks 1..WK-1, summed through the stage of the last step
-  static constexpr int COMB = (WK - 1) * WQ * 32 * D * 4;
-  static constexpr bool COMB_IN_STAGE = COMB <= STAGE;
-  static constexpr int SMEM = 2 * STAGE + (COMB_IN_STAGE ? 0 : COMB);
-  static constexpr int BIAS_ROWS = BM * (BN / 64);
+  // dQ^T partials of key blocks 1..WK-1: one pass through a region of their
+  // own when the LDS budget allows, else DP 32-column blocks of D per pass
+  // through the stage of the unit's last step
+  static constexpr int COMB_PER_D = (WK - 1) * WQ * 32 * 32 * 4;
+  static constexpr int COMB = COMB_PER_D * ND;
+  static constexpr bool COMB_IN_STAGE = WK > 1 && 2 * STAGE + COMB > 160 * 1024;
+  static constexpr int DP_FIT = STAGE / COMB_PER_D;
+  static_assert(!COMB_IN_STAGE || DP_FIT >= 1, "combine pass does not fit a stage");
+  static constexpr int DP = !COMB_IN_STAGE || DP_FIT >= ND ? ND : (DP_FIT >= 2 && ND % 2 == 0 ? 2 : 1);
+  static constexpr int SMEM = 2 * STAGE + (WK > 1 && !COMB_IN_STAGE ? COMB : 0);
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(!BIAS || (BIAS_ROWS % NW == 0 && NW % (BN / 64) == 0), "bias segments must deal evenly");
 };
 
 template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
@@ -67,15 +74,17 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   auto stage_b = [&](int s) { return smem + s * Sh::STAGE + Sh::K_BYTES + Sh::V_BYTES; };
   const uint32_t smem_lds = lds_addr(smem);
 
-  RowLoader<D, 2, BN, NW> kload;
-  RowLoader<D, 1, BN, NW> vload;
+  // K/V rows permuted only when a bias tile is read (see the header)
+  RowLoader<D, 2, BN, NW, BIAS> kload;
+  RowLoader<D, 1, BN, NW, BIAS> vload;
+  BiasLoader<BN, 1, BM, NW> bload;
   kload.init(wave, lane, HD);
   vload.init(wave, lane, HD);
 
   struct UnitInfo {
     int h, qt, n;
     Sample s;
-    i32x4 rk, rv, rb;
+    i32x4 rk, rv;
   };
   auto fetch = [&](int u) {
     UnitInfo x;
@@ -87,10 +96,13 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
     const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D;
     x.rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + kvo, 0);
     x.rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + kvo, 0);
-    if constexpr (BIAS)
-      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk, 0);
     return x;
   };
+  // First element of the unit's (sample, head) bias block.  Derived where it
+  // is needed rather than kept in the unit record: state copied between
+  // units that a compiler cannot keep in registers lands in scratch, whose
+  // accesses wait on vmcnt and with it on the LDS prefetches.
+  auto bias_elem0 = [&](const UnitInfo& x) { return x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk; };
   auto issue_step = [&](const UnitInfo& x, int t, int st) {
     const uint32_t sb = smem_lds + st * Sh::STAGE;
     const int64_t row0 = (int64_t)t * BN;
@@ -98,22 +110,12 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
     kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
     vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
     if constexpr (BIAS) {
-      // one 64-key segment of one query row per load, lane l -> key l
-      constexpr int SEGS = BN / 64, RSTEP = NW / SEGS;
-      const int cc = wave % SEGS, c0 = t * BN + cc * 64;
-      const int nk = max(min(x.s.lk - c0, 64), 0) * 2;
-      int qr = x.qt * BM + wave / SEGS;
-      i32x4 rb = rsrc_at(x.rb, ((int64_t)qr * x.s.lk + c0) * 2, 0);
-      uint32_t m0 = sb + Sh::K_BYTES + Sh::V_BYTES + (wave / SEGS) * Sh::BROW + cc * 256;
-      const int64_t row_bytes = (int64_t)RSTEP * x.s.lk * 2;
-#pragma unroll
-      for (int j = 0; j < Sh::BIAS_ROWS / NW; ++j) {
-        rb[2] = qr < x.s.lq ? nk : 0;
-        lds_dma2(rb, m0, lane * 2);
-        rb = rsrc_at(rb, row_bytes, 0);
-        m0 += RSTEP * Sh::BROW;
-        qr += RSTEP;
-      }
+      // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
+      if (t == 0) bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = bias_elem0(x);
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + (int64_t)t * BN) * 2;
+      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
+      bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
     }
   };
   // Q and dO fragments (B operands) and row statistics of this lane's query row
@@ -193,16 +195,22 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
       }
       if (t + 1 == n && has_next) load_do(nxt, dof, lse2, di);
 
+      // with a bias, slot i of this lane holds key t*BN + kb + 16g + i of
+      // query row qt*BM + wq*32 + l32 (else key t*BN + kb + acc_row(i, g))
       float ds[16];
+      const int rem = cur.s.lk - (t * BN + kb + (BIAS ? 16 * g : 0));  // keys >= lk: slot key >= rem
       if constexpr (BIAS) {
-        const char* bt = stage_b(stage);
-        const int r = wq * 32 + l32;
+        const char* bt = stage_b(stage) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
+        bf16x8_to_f32(bt, ds);
+        bf16x8_to_f32(bt + 16, ds + 8);
+        if (t + 1 == n && bias_elem0(cur) + (int64_t)cur.s.lq * cur.s.lk == a.bias_elems) {
+          // the tensor's last element may straddle the end of the bias range
+          // by half a dword, which the range check drops: reload it
+          const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(a.bias) + (a.bias_elems - 1), 2);
+          const float last = __uint_as_float((uint32_t)buf_load2(rl, 0) << 16);
+          const int row = cur.qt * BM + wq * 32 + l32;
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int c = kb + a4 * 8 + g * 4;  // 4 consecutive keys
-          const u32x4 w = *reinterpret_cast<const u32x4*>(bt + r * Sh::BROW + c * 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ds[a4 * 4 + j] = __uint_as_float(w[j] << 16);
+          for (int i = 0; i < 16; ++i) ds[i] = (row == cur.s.lq - 1 && i == rem - 1) ? last : ds[i];
         }
       }
       if constexpr (SOFTMAX) {
@@ -218,6 +226,12 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
           const float x = BIAS ? fmaf(sacc[i], a.scale, ds[i]) : sacc[i] * a.scale;
           ds[i] = act_grad(ACT, x) * dpacc[i];
         }
+      }
+      if (t + 1 == n) {
+        // keys past the sample end (zero K/V rows, bias of the next row): their
+        // dS must be exactly zero, whatever P overflowed to
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = (BIAS ? i : acc_row(i, g)) < rem ? ds[i] : 0.0f;
       }
 
 #pragma unroll
@@ -250,22 +264,26 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
         float* po = reinterpret_cast<float*>(Sh::COMB_IN_STAGE ? smem + (stage ^ 1) * Sh::STAGE
                                                                : smem + 2 * Sh::STAGE);
         const int lane_off = g * 4 * 32 + l32;
-        if (wk > 0) {
-          float* pw = po + ((wk - 1) * WQ + wq) * D * 32 + lane_off;
 #pragma unroll
-          for (int d = 0; d < ND; ++d)
+        for (int d0 = 0; d0 < ND; d0 += Sh::DP) {
+          if (d0 > 0) __syncthreads();  // the previous pass has been read
+          if (wk > 0) {
+            float* pw = po + ((wk - 1) * WQ + wq) * Sh::DP * 32 * 32 + lane_off;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) pw[(d * 32 + (i >> 2) * 8 + (i & 3)) * 32] = dqacc[d][i];
-        }
-        __syncthreads();
-        if (wk == 0) {
+            for (int dl = 0; dl < Sh::DP; ++dl)
 #pragma unroll
-          for (int w2 = 1; w2 < WK; ++w2) {
-            const float* pr = po + ((w2 - 1) * WQ + wq) * D * 32 + lane_off;
+              for (int i = 0; i < 16; ++i) pw[(dl * 32 + (i >> 2) * 8 + (i & 3)) * 32] = dqacc[d0 + dl][i];
+          }
+          __syncthreads();
+          if (wk == 0) {
 #pragma unroll
-            for (int d = 0; d < ND; ++d)
+            for (int w2 = 1; w2 < WK; ++w2) {
+              const float* pr = po + ((w2 - 1) * WQ + wq) * Sh::DP * 32 * 32 + lane_off;
 #pragma unroll
-              for (int i = 0; i < 16; ++i) dqacc[d][i] += pr[(d * 32 + (i >> 2) * 8 + (i & 3)) * 32];
+              for (int dl = 0; dl < Sh::DP; ++dl)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dqacc[d0 + dl][i] += pr[(dl * 32 + (i >> 2) * 8 + (i & 3)) * 32];
+            }
           }
         }
       }

@@ -16,9 +16,14 @@
 // K, V and the bias tile travel HBM -> LDS with buffer loads whose
 // destination is LDS (no registers, rows past the sample end read as zero),
 // double-buffered so that step t+1 (or the next unit's first step) loads
-// while step t computes; one barrier per step.  The key-split partials of
-// one query group are combined through LDS at the end of a unit.
+// while step t computes; one barrier per step.  K and V rows are stored
+// permuted within each 32-key block (RowLoader PERM), which makes the 16
+// scores a lane holds 16 consecutive keys: the lane's bias values are then
+// two aligned 16-byte LDS reads.  The key-split partials of one query group
+// are combined through LDS at the end of a unit.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
@@ -38,18 +43,25 @@ struct Fwd2Shape {
   using VT = PadTile<D, 2>;  // V rows: pitch = 32 (mod 256) bytes, for transposed reads
   static constexpr int K_BYTES = KT::template bytes<BN>();
   static constexpr int V_BYTES = VT::template bytes<BN>();
-  static constexpr int BROW = BN * 4 + 16;     // bias row: BN 4-byte slots + pad
-  static constexpr int B_BYTES = BIAS ? BM * BROW : 0;
+  using BT = PadTile<BN, 1>;  // bias rows: pitch = 16 (mod 256) bytes, 16-byte reads conflict-free
+  static constexpr int B_BYTES = BIAS ? BT::template bytes<BM>() : 0;
   static constexpr int STAGE = K_BYTES + V_BYTES + B_BYTES;
-  static constexpr int COMB_O = (WK - 1) * WQ * 32 * D * 4;  // partial O of key halves 1..WK-1
-  static constexpr int STATS = (WK - 1) * WQ * 32 * 3 * 4;   // their m, l, l_rounded
-  static constexpr bool O_IN_STAGE = (WK > 1) && STAGE >= COMB_O;
-  static constexpr bool S_IN_STAGE = (WK > 1) && STAGE >= COMB_O + STATS;
-  static constexpr int EXTRA = (WK > 1) ? ((O_IN_STAGE ? 0 : COMB_O) + (S_IN_STAGE ? 0 : STATS)) : 0;
+  // The key-split partials of O (key blocks 1..WK-1) are summed through the
+  // stage of the unit's last step, DP 32-column blocks of D per pass; their
+  // m, l, l_rounded go first.
+  static constexpr int STATS = (WK - 1) * WQ * 32 * 3 * 4;
+  static constexpr int COMB_PER_D = (WK - 1) * WQ * 32 * 32 * 4;
+  static constexpr int DP_FIT = WK > 1 ? (STAGE - STATS) / COMB_PER_D : ND;
+  // One pass through a region of its own when the LDS budget allows (no
+  // extra barriers: short-key units are often a single step), else passes
+  // through the free stage.
+  static constexpr int OWN = STATS + COMB_PER_D * ND;
+  static constexpr bool COMB_IN_STAGE = WK > 1 && 2 * STAGE + OWN > 160 * 1024;
+  static_assert(!COMB_IN_STAGE || DP_FIT >= 1, "combine pass does not fit a stage");
+  static constexpr int DP = !COMB_IN_STAGE || DP_FIT >= ND ? ND : (DP_FIT >= 2 && ND % 2 == 0 ? 2 : 1);
+  static constexpr int EXTRA = (WK > 1 && !COMB_IN_STAGE) ? OWN : 0;
   static constexpr int SMEM = 2 * STAGE + EXTRA;
-  static constexpr int BIAS_ROWS = BM * (BN / 64);  // 64-key bias row segments per step
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(!BIAS || (BIAS_ROWS % NW == 0 && NW % (BN / 64) == 0), "bias segments must deal evenly");
 };
 
 template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
@@ -73,15 +85,17 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   auto stage_b = [&](int s) { return smem + s * Sh::STAGE + Sh::K_BYTES + Sh::V_BYTES; };
   const uint32_t smem_lds = lds_addr(smem);
 
-  RowLoader<D, 1, BN, NW> kload;
-  RowLoader<D, 2, BN, NW> vload;
+  // K/V rows permuted only when a bias tile is read (see the header)
+  RowLoader<D, 1, BN, NW, BIAS> kload;
+  RowLoader<D, 2, BN, NW, BIAS> vload;
+  BiasLoader<BN, 1, BM, NW> bload;
   kload.init(wave, lane, HD);
   vload.init(wave, lane, HD);
 
   struct UnitInfo {
     int b, h, qt, n;
     Sample s;
-    i32x4 rk, rv, rb;  // descriptors at row 0 of this (sample, head)
+    i32x4 rk, rv;  // descriptors at row 0 of this (sample, head)
   };
   auto fetch = [&](int u) {
     UnitInfo x;
@@ -94,10 +108,13 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D;
     x.rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + kvo, 0);
     x.rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + kvo, 0);
-    if constexpr (BIAS)
-      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk, 0);
     return x;
   };
+  // First element of the unit's (sample, head) bias block.  Derived where it
+  // is needed rather than kept in the unit record: state copied between
+  // units that a compiler cannot keep in registers lands in scratch, whose
+  // accesses wait on vmcnt and with it on the LDS prefetches.
+  auto bias_elem0 = [&](const UnitInfo& x) { return x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk; };
   // issue the HBM -> LDS loads of step t of unit x into stage st: the K and V
   // descriptors start at the step's first key row and end at the sample end
   auto issue_step = [&](const UnitInfo& x, int t, int st) {
@@ -107,24 +124,12 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
     vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
     if constexpr (BIAS) {
-      // one 64-key segment of one query row per load, lane l -> key l; the
-      // descriptor covers exactly the valid part of the segment.  A wave
-      // keeps one segment column and walks down the rows.
-      constexpr int SEGS = BN / 64, RSTEP = NW / SEGS;
-      const int cc = wave % SEGS, c0 = t * BN + cc * 64;
-      const int nk = max(min(x.s.lk - c0, 64), 0) * 2;
-      int qr = x.qt * BM + wave / SEGS;
-      i32x4 rb = rsrc_at(x.rb, ((int64_t)qr * x.s.lk + c0) * 2, 0);
-      uint32_t m0 = sb + Sh::K_BYTES + Sh::V_BYTES + (wave / SEGS) * Sh::BROW + cc * 256;
-      const int64_t row_bytes = (int64_t)RSTEP * x.s.lk * 2;
-#pragma unroll
-      for (int j = 0; j < Sh::BIAS_ROWS / NW; ++j) {
-        rb[2] = qr < x.s.lq ? nk : 0;
-        lds_dma2(rb, m0, lane * 2);
-        rb = rsrc_at(rb, row_bytes, 0);
-        m0 += RSTEP * Sh::BROW;
-        qr += RSTEP;
-      }
+      // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
+      if (t == 0) bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = bias_elem0(x);
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + (int64_t)t * BN) * 2;
+      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
+      bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
     }
   };
   // Q fragments (B operand) of this wave's 32 rows, straight into registers
@@ -155,7 +160,11 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
     float m_run = 0.0f, l_run = 0.0f, lr_run = 0.0f;
 
-    for (int t = 0; t < n; ++t) {
+    // One K/V step.  FIRST (step 0) starts the running max at the step's
+    // max; later steps rescale lazily.  Separate instances keep the
+    // accumulators in place across the rescale branch.
+    auto step = [&](auto first_tag, int t) {
+      constexpr bool FIRST = decltype(first_tag)::value;
       wait_vmcnt0();
       __syncthreads();  // step t is in LDS; every wave is done with step t-1
       if (t + 1 < n) {
@@ -173,16 +182,28 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       // Q is dead after the last S^T of the unit: fetch the next unit's rows
       if (t + 1 == n && has_next) load_q(nxt, qf);
 
+      // with a bias, slot i of this lane holds key t*BN + kb + 16g + i of
+      // query row qt*BM + wq*32 + l32 (else key t*BN + kb + acc_row(i, g))
       float p[16];
       if constexpr (BIAS) {
-        const char* bt = stage_b(stage);
-        const int r = wq * 32 + l32;
+        const char* bt = stage_b(stage) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
+        bf16x8_to_f32(bt, p);
+        bf16x8_to_f32(bt + 16, p + 8);
+        if (t + 1 == n) {
+          // keys past the sample end carry the next row's bias: they must add
+          // nothing (the subtraction below assumes a zero score)
+          const int rem = cur.s.lk - (t * BN + kb + 16 * g);
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int c = kb + a4 * 8 + g * 4;  // 4 consecutive keys
-          const u32x4 w = *reinterpret_cast<const u32x4*>(bt + r * Sh::BROW + c * 4);
+          for (int i = 0; i < 16; ++i) p[i] = i < rem ? p[i] : 0.0f;
+          if (bias_elem0(cur) + (int64_t)cur.s.lq * cur.s.lk == a.bias_elems) {
+            // the tensor's last element may straddle the end of the bias
+            // range by half a dword, which the range check drops: reload it
+            const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(a.bias) + (a.bias_elems - 1), 2);
+            const float last = __uint_as_float((uint32_t)buf_load2(rl, 0) << 16);
+            const int row = cur.qt * BM + wq * 32 + l32;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[a4 * 4 + j] = __uint_as_float(w[j] << 16);
+            for (int i = 0; i < 16; ++i) p[i] = (row == cur.s.lq - 1 && i == rem - 1) ? last : p[i];
+          }
         }
       }
       bf16x8 pf[2], pl[2];
@@ -196,21 +217,23 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           mx = fmaxf(mx, p[i]);
         }
         mx = wave_xor32_max(mx);
-        if (t == 0) {
-          // first step: the running max starts at this step's max (m_run was 0)
+        if constexpr (FIRST) {
+          // the running max starts at this step's max (m_run was 0)
           m_run = mx;
 #pragma unroll
           for (int i = 0; i < 16; ++i) p[i] -= mx;
-        } else if (__builtin_amdgcn_ballot_w64(mx > kLazy) != 0) {
-          const float delta = fmaxf(mx, 0.0f);
-          const float alpha = fast_exp2(-delta);
-          l_run *= alpha;
-          lr_run *= alpha;
+        } else {
+          if (__builtin_amdgcn_ballot_w64(mx > kLazy) != 0) {
+            const float delta = fmaxf(mx, 0.0f);
+            const float alpha = fast_exp2(-delta);
+            l_run *= alpha;
+            lr_run *= alpha;
 #pragma unroll
-          for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
-          m_run += delta;
+            for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+            m_run += delta;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) p[i] -= delta;
+            for (int i = 0; i < 16; ++i) p[i] -= delta;
+          }
         }
         float rs = 0.0f, rsr = 0.0f;
 #pragma unroll
@@ -260,6 +283,10 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         }
       }
       stage ^= 1;
+    };
+    if (n > 0) {
+      step(std::true_type{}, 0);
+      for (int t = 1; t < n; ++t) step(std::false_type{}, t);
     }
 
     // ---- epilogue ----
@@ -286,55 +313,64 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     if constexpr (WK > 1) {
       // stage that held the last step is free once every wave passes this barrier
       __syncthreads();
-      char* free_stage = smem + (stage ^ 1) * Sh::STAGE;
-      float* po = reinterpret_cast<float*>(Sh::O_IN_STAGE ? free_stage : smem + 2 * Sh::STAGE);
-      float* ps = reinterpret_cast<float*>(Sh::S_IN_STAGE ? free_stage + Sh::COMB_O
-                                                          : smem + 2 * Sh::STAGE + (Sh::O_IN_STAGE ? 0 : Sh::COMB_O));
-      // element (row r of the 32-column block d, query l32) of a partial sits
-      // at [slot][d*32 + r][l32]; lane-dependent parts go into one base
+      char* free_stage = Sh::COMB_IN_STAGE ? smem + (stage ^ 1) * Sh::STAGE : smem + 2 * Sh::STAGE;
+      float* ps = reinterpret_cast<float*>(free_stage);
+      float* po = reinterpret_cast<float*>(free_stage + Sh::STATS);
+      // element (row r of the 32-column block dl of a pass, query l32) of a
+      // partial sits at [slot][dl*32 + r][l32]; lane-dependent parts go into one base
       const int lane_off = g * 4 * 32 + l32;
-      if (wk > 0) {
-        const int slot = (wk - 1) * WQ + wq;
-        float* pw = po + slot * D * 32 + lane_off;
+      float fw[WK];  // weight of each key block's partial (block 0 = this wave)
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+      for (int d0 = 0; d0 < ND; d0 += Sh::DP) {
+        if (d0 > 0) __syncthreads();  // the previous pass has been read
+        if (wk > 0) {
+          const int slot = (wk - 1) * WQ + wq;
+          float* pw = po + slot * Sh::DP * 32 * 32 + lane_off;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pw[(d * 32 + (i >> 2) * 8 + (i & 3)) * 32] = oacc[d][i];
-        if (g == 0) {
-          ps[(slot * 3 + 0) * 32 + l32] = m_run;
-          ps[(slot * 3 + 1) * 32 + l32] = l_run;
-          ps[(slot * 3 + 2) * 32 + l32] = lr_run;
-        }
-      }
-      __syncthreads();
-      if (wk == 0) {
-        float mall = m_run;
-        if constexpr (SOFTMAX) {
+          for (int dl = 0; dl < Sh::DP; ++dl)
 #pragma unroll
-          for (int w2 = 1; w2 < WK; ++w2) mall = fmaxf(mall, ps[(((w2 - 1) * WQ + wq) * 3) * 32 + l32]);
-        }
-        const float f0 = SOFTMAX ? (has_keys ? fast_exp2(m_run - mall) : 0.0f) : 1.0f;
-        float lall = l_run * f0, lrall = lr_run * f0;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) oacc[d] *= f0;
-#pragma unroll
-        for (int w2 = 1; w2 < WK; ++w2) {
-          const int slot = (w2 - 1) * WQ + wq;
-          float f = 1.0f;
-          if constexpr (SOFTMAX) {
-            f = has_keys ? fast_exp2(ps[(slot * 3) * 32 + l32] - mall) : 0.0f;
-            lall += ps[(slot * 3 + 1) * 32 + l32] * f;
-            lrall += ps[(slot * 3 + 2) * 32 + l32] * f;
+            for (int i = 0; i < 16; ++i) pw[(dl * 32 + (i >> 2) * 8 + (i & 3)) * 32] = oacc[d0 + dl][i];
+          if (d0 == 0 && g == 0) {
+            ps[(slot * 3 + 0) * 32 + l32] = m_run;
+            ps[(slot * 3 + 1) * 32 + l32] = l_run;
+            ps[(slot * 3 + 2) * 32 + l32] = lr_run;
           }
-          const float* pr = po + slot * D * 32 + lane_off;
-#pragma unroll
-          for (int d = 0; d < ND; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[d][i] += f * pr[(d * 32 + (i >> 2) * 8 + (i & 3)) * 32];
         }
-        m_run = mall;
-        l_run = lall;
-        lr_run = lrall;
+        __syncthreads();
+        if (wk == 0) {
+          if (d0 == 0) {
+            float mall = m_run;
+            if constexpr (SOFTMAX) {
+#pragma unroll
+              for (int w2 = 1; w2 < WK; ++w2) mall = fmaxf(mall, ps[(((w2 - 1) * WQ + wq) * 3) * 32 + l32]);
+            }
+            fw[0] = SOFTMAX ? (has_keys ? fast_exp2(m_run - mall) : 0.0f) : 1.0f;
+            float lall = l_run * fw[0], lrall = lr_run * fw[0];
+#pragma unroll
+            for (int w2 = 1; w2 < WK; ++w2) {
+              const int slot = (w2 - 1) * WQ + wq;
+              fw[w2] = 1.0f;
+              if constexpr (SOFTMAX) {
+                fw[w2] = has_keys ? fast_exp2(ps[(slot * 3) * 32 + l32] - mall) : 0.0f;
+                lall += ps[(slot * 3 + 1) * 32 + l32] * fw[w2];
+                lrall += ps[(slot * 3 + 2) * 32 + l32] * fw[w2];
+              }
+            }
+            m_run = mall;
+            l_run = lall;
+            lr_run = lrall;
+          }
+#pragma unroll
+          for (int dl = 0; dl < Sh::DP; ++dl) oacc[d0 + dl] *= fw[0];
+#pragma unroll
+          for (int w2 = 1; w2 < WK; ++w2) {
+            const float* pr = po + ((w2 - 1) * WQ + wq) * Sh::DP * 32 * 32 + lane_off;
+#pragma unroll
+            for (int dl = 0; dl < Sh::DP; ++dl)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) oacc[d0 + dl][i] += fw[w2] * pr[(dl * 32 + (i >> 2) * 8 + (i & 3)) * 32];
+          }
+        }
       }
     }
 

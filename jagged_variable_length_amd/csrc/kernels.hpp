@@ -26,6 +26,7 @@ struct FwdArgs {
   int H;
   float scale;       // softmax / activation scale
   float scale_log2;  // scale * log2(e)
+  int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
 };
 
 struct DiArgs {
@@ -56,6 +57,7 @@ struct BwdArgs {
   int H;
   float scale;
   float scale_log2;
+  int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
 };
 
 // Which template instance to run.

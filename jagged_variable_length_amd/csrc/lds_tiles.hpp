@@ -26,10 +26,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Descriptor moved `bytes_off` bytes forward with `records` bytes left
-// (records <= 0 -> every load of it reads zero).  Scalar arithmetic only.
+// (records <= 0 -> every load of it reads zero).  Records are capped below
+// 2^31, so the 0x80000000 offset that marks a pad lane is always out of
+// range.  Scalar arithmetic only.
 __device__ __forceinline__ i32x4 rsrc_at(const i32x4& r, int64_t bytes_off, int64_t records) {
   const uint64_t p = ((uint64_t)(uint32_t)r[0] | ((uint64_t)(uint32_t)r[1] << 32)) + (uint64_t)bytes_off;
-  const int64_t n = records < 0 ? 0 : records;
+  const int64_t n = records < 0 ? 0 : (records > 0x7fffffff ? 0x7fffffff : records);
   return i32x4{(int)(uint32_t)p, (int)(uint32_t)(p >> 32), (int)(uint32_t)n, r[3]};
 }
 
@@ -75,7 +77,12 @@ struct PadTile {
 // only on the row pitch in HBM (H*D elements), so they are computed once; a
 // step only moves the scalar descriptor (rsrc_at) to its first row, and rows
 // at or past the descriptor end arrive as zeros.
-template <int D, int PAD, int ROWS, int NPARTS>
+// PERM: tile row m of every 32-row block holds source row perm32(m) of that
+// block.  Read as an MFMA A operand in tile order, such a tile makes the
+// accumulator of lane half g hold rows 16g .. 16g+15 of the block in slot
+// order (perm32(acc_row(i, g)) = 16g + i), and the transposed reads in
+// accumulator order (trans_frag) deliver source rows in plain order.
+template <int D, int PAD, int ROWS, int NPARTS, bool PERM = false>
 struct RowLoader {
   using T = PadTile<D, PAD>;
   static constexpr int NI = T::template ninst<ROWS>();
@@ -86,7 +93,8 @@ struct RowLoader {
     for (int j = 0; j < NJ; ++j) {
       const int slot = (part + j * NPARTS) * 64 + lane;
       const int rr = slot / T::SPR, ch = slot % T::SPR;
-      voff[j] = (ch < T::CPR && rr < ROWS) ? (uint32_t)(rr * HD + ch * 8) * 2 : 0x80000000u;
+      const int src = PERM ? ((rr & ~31) | perm32(rr & 31)) : rr;
+      voff[j] = (ch < T::CPR && rr < ROWS) ? (uint32_t)(src * HD + ch * 8) * 2 : 0x80000000u;
     }
   }
   // part must be wave-uniform; tile is the LDS byte address of the tile
@@ -98,6 +106,47 @@ struct RowLoader {
     }
   }
 };
+
+// Bias tile: ROWS rows x COLS keys of one (sample, head) bias block, whose
+// rows are lk elements apart in HBM at any 2-byte alignment.  Each row is
+// moved as COLS/8 unaligned 16-byte loads (the code-object ABI of this
+// target runs with unaligned buffer access enabled, and the range check is
+// per dword) into a PadTile<COLS, PAD>, so the tile holds plain bf16 rows at
+// 16-byte aligned positions.  Loads past the descriptor end read as zero;
+// keys at or past lk carry the next row's values and are masked by the
+// kernels.  The offsets depend on lk, so they are rebuilt per unit.
+template <int COLS, int PAD, int ROWS, int NPARTS>
+struct BiasLoader {
+  using T = PadTile<COLS, PAD>;
+  static constexpr int NI = T::template ninst<ROWS>();
+  static constexpr int NJ = (NI + NPARTS - 1) / NPARTS;
+  uint32_t voff[NJ];
+  __device__ __forceinline__ void init(int part, int lane, int lk) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int slot = (part + j * NPARTS) * 64 + lane;
+      const int rr = slot / T::SPR, ch = slot % T::SPR;
+      voff[j] = (ch < T::CPR && rr < ROWS) ? (uint32_t)(rr * lk + ch * 8) * 2 : 0x80000000u;
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t tile, const i32x4& r, int part) const {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int inst = part + j * NPARTS;
+      if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, voff[j]);
+    }
+  }
+};
+
+// Eight consecutive bf16 (one aligned 16-byte LDS read) widened to fp32.
+__device__ __forceinline__ void bf16x8_to_f32(const char* p, float* out) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(w[j] << 16);
+    out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
 
 // B/A fragment of a row operand: 8 bf16 of row `row`, columns kk*16 + g*8 ..
 template <int D, int PAD>
