@@ -212,8 +212,9 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
-    // the bf16 dK/dV kernel has no room for a bias tile with 128-query steps at D = 128
-    if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias && p->dkdv_wkv == 1) p->dkdv_wkv = 2;
+    // the bf16 dK/dV kernel keeps three or four step stages in LDS: 128-query
+    // steps (32-key units) do not leave room for three at D = 128
+    if (d.in_dtype == JATTN_BF16 && d.D == 128 && p->dkdv_wkv == 1) p->dkdv_wkv = 2;
     const int dkdv_tile = 32 * p->dkdv_wkv, dkdv_step = 32 * (4 / p->dkdv_wkv);
     jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd);
     jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq);

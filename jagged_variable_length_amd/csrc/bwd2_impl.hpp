@@ -19,13 +19,18 @@
 // dV/dK products without reshuffling (the accumulator rows are queries in the
 // order that the transposed reads deliver).
 //
+// Software pipeline (one wave per SIMD, so nothing else hides latency): the
+// S/dP MFMAs of step t+1 are issued interleaved with the VALU work of step t
+// (P, dS, dBias), then the dV/dK MFMAs of step t.  A unit starts with the
+// S/dP of its step 0 and ends with a step that has no successor.
+//
 // Memory pipeline: Q, dO, the bias tile and the row statistics of a step go
-// HBM -> LDS with buffer loads whose destination is LDS, NS steps deep (a
-// ring of stages; step c + NS - 1 is issued while step c computes, also
-// across unit boundaries).  K and V of a unit live in registers; the next
-// unit's K/V are loaded during the last step of the current unit, right
-// after their last use.  Each wait counts only the loads issued after the data it
-// needs (loads return in order), so the prefetches stay in flight.
+// HBM -> LDS with buffer loads whose destination is LDS, into a ring of NS
+// stages (NS - 2 steps ahead of the step being acquired, also across unit
+// boundaries).  K and V of a unit live in registers; the next unit's K/V are
+// loaded right after their last S/dP use.  Vector memory operations complete
+// in issue order, so each wait lets every operation issued after the needed
+// loads stay in flight (exact per-wave counts, dBias stores included).
 #pragma once
 #include "common.hpp"
 #include "fwd_impl.hpp"
@@ -63,12 +68,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// 16-byte register load issued as inline asm: the compiler does not track it,
-// the kernel waits for it explicitly (see the unit switch below).
-__device__ __forceinline__ void asm_load16(bf16x8& dst, const i32x4& r, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(voff), "s"(r) : "memory");
-}
-
 template <int D, int WKV, int WKQ, bool SOFTMAX, bool BIAS>
 struct Dkdv2Shape {
   static constexpr int NW = WKV * WKQ;
@@ -91,24 +90,59 @@ struct Dkdv2Shape {
   // the unit's last step, which is free once every wave has computed it
   static constexpr int COMB = WKQ > 1 ? (WKQ - 1) * WKV * D * 32 * 4 : 0;
   static constexpr int NS_FIT = 160 * 1024 / STAGE;
-  static constexpr int NS = NS_FIT >= 3 ? 3 : 2;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : 3;
   static constexpr int SMEM = NS * STAGE;
-  // loads that every wave issues per step (the minimum over waves)
   static constexpr int QNI = QT::template ninst<QS>();
-  static constexpr int L_MIN =
-      2 * (QNI / NW) + (BIAS ? BT::template ninst<QS>() / NW : 0) + (NRS >= NW ? NRS / NW : 0);
-  static_assert(NS_FIT >= 2 && COMB <= STAGE, "LDS budget");
+  static constexpr int BNI = BIAS ? BT::template ninst<QS>() : 0;
+  static_assert(NS_FIT >= 3 && COMB <= STAGE, "LDS budget");
   static_assert(NW == 4, "four waves");
-  static_assert(L_MIN < 64, "vmcnt range");
 };
+
+// Number of the NI load instructions part, part + NP, ... that wave `part` issues.
+__device__ __forceinline__ constexpr int loads_of(int NI, int part, int NP) {
+  return part < NI ? (NI - part + NP - 1) / NP : 0;
+}
+
+// s_waitcnt vmcnt(n) for a runtime n (clamped to 0..63): binary dispatch to
+// compile-time immediates.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID)
+      wait_vmcnt_le<MID, HI>(n);
+    else
+      wait_vmcnt_le<LO, MID - 1>(n);
+  }
+}
 
 // DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
 template <typename TG, int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv2_kernel(BwdArgs a) {
+  // Argument fields as locals: the lambdas below capture by reference, and a
+  // reference to the argument block itself would keep it in scratch memory.
+  const void* const A_q = a.q;
+  const void* const A_k = a.k;
+  const void* const A_v = a.v;
+  const void* const A_bias = a.bias;
+  const void* const A_dout = a.dout;
+  const float* const A_di = a.di;
+  const float* const A_lse2 = a.lse2;
+  void* const A_dk = a.dk;
+  void* const A_dv = a.dv;
+  void* const A_dbias = a.dbias;
+  const int32_t* const A_units = a.units;
+  const int32_t* const A_samples = a.samples;
+  const int A_H = a.H;
+  const float A_scale = a.scale;
+  const float A_scale_log2 = a.scale_log2;
+  const int64_t A_bias_elems = a.bias_elems;
   constexpr bool SOFTMAX = (ACT == kSoftmax);
   using Sh = Dkdv2Shape<D, WKV, WKQ, SOFTMAX, BIAS>;
   constexpr int NW = Sh::NW, KT = Sh::KT, QS = Sh::QS, ND = D / 32, NKK = D / 16, NS = Sh::NS;
-  constexpr int PAD = Sh::PAD, L = Sh::L_MIN;
+  constexpr int PAD = Sh::PAD;
   constexpr int ESB = DBIAS == 2 ? 4 : 2;  // dBias element size
 
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
@@ -119,50 +153,38 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
   const int u_begin = sload1(a.worker_off, worker);
   const int u_end = sload1(a.worker_off, worker + 1);
-  const int H = a.H, HD = a.H * D;
+  const int H = A_H, HD = A_H * D;
 
   RowLoader<D, PAD, QS, NW> qload;
   BiasLoader<KT, 1, QS, NW> bload;
   qload.init(wave, lane, HD);
   const uint32_t rs_voff = (uint32_t)lane * H * 4;  // row-stat load: lane l -> query row l of the load
 
+  // Unit record: sample fields only.  Buffer descriptors are rebuilt where
+  // they are used (a few scalar operations): three records are live at once
+  // (producer, consumer, next), and descriptors in them would spill SGPRs.
   struct Unit {
     int h, kt, n;
     Sample s;
-    i32x4 rq, rdo, rl, rd, rb;  // descriptors at query row 0 of the (sample, head)
-    int64_t brec;               // bytes from the bias block start to the end of the bias tensor
-    bool tail;                  // the bias block holds the tensor's last element
   };
-  auto fetch = [&](int u) {
-    Unit x{};
-    const i32x4 un = sload4(a.units, u);
+  auto fetch = [&](int u) __attribute__((always_inline)) {
+    Unit x;
+    const i32x4 un = sload4(A_units, u);
     x.h = un[1];
     x.kt = un[2];
     x.n = un[3];
-    x.s = sload_sample(a.samples, un[0]);
-    const int64_t qo = ((int64_t)x.s.q0 * H + x.h) * D;
-    x.rq = rsrc_words(reinterpret_cast<const bf16*>(a.q) + qo, 0);
-    x.rdo = rsrc_words(reinterpret_cast<const bf16*>(a.dout) + qo, 0);
-    if constexpr (SOFTMAX) {
-      x.rl = rsrc_words(a.lse2 + (int64_t)x.s.q0 * H + x.h, 0);
-      x.rd = rsrc_words(a.di + (int64_t)x.s.q0 * H + x.h, 0);
-    }
-    if constexpr (BIAS) {
-      const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
-      x.rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
-      x.brec = (a.bias_elems - e0) * 2;
-      x.tail = e0 + (int64_t)x.s.lq * x.s.lk == a.bias_elems;
-    }
+    x.s = sload_sample(A_samples, un[0]);
     return x;
   };
 
   // ---- producer: HBM -> LDS loads of one step into one stage ----
-  auto issue_step = [&](const Unit& x, int t, int st) {
+  auto issue_step = [&](const Unit& x, int t, int st) __attribute__((always_inline)) {
     const uint32_t sb = smem_lds + st * Sh::STAGE;
     const int r0 = t * QS;
     const int64_t rec = (int64_t)(x.s.lq - r0) * HD * 2;
-    qload.issue(sb, rsrc_at(x.rq, (int64_t)r0 * HD * 2, rec), wave);
-    qload.issue(sb + Sh::OFF_O, rsrc_at(x.rdo, (int64_t)r0 * HD * 2, rec), wave);
+    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D;  // first row of the step
+    qload.issue(sb, rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_q) + qo, 0), 0, rec), wave);
+    qload.issue(sb + Sh::OFF_O, rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_dout) + qo, 0), 0, rec), wave);
     if constexpr (SOFTMAX) {
       // load j: rows 64*(j % (NRS/2)) .. of LSE (j < NRS/2) or Di
       constexpr int HALF = Sh::NRS / 2;
@@ -171,18 +193,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int jj = j + wave;
         if (jj < Sh::NRS) {
           const int rr = r0 + 64 * (jj % HALF);
-          const i32x4 base = jj < HALF ? x.rl : x.rd;
+          const float* rs = (jj < HALF ? A_lse2 : A_di) + ((int64_t)(x.s.q0 + rr) * H + x.h);
           const uint32_t voff = 64 * (jj % HALF) + lane < QS ? rs_voff : 0x80000000u;
-          lds_dma4(rsrc_at(base, (int64_t)rr * H * 4, (int64_t)(x.s.lq - rr) * H * 4),
-                   sb + Sh::OFF_RS + jj * 256, voff);
+          lds_dma4(rsrc_at(rsrc_words(rs, 0), 0, (int64_t)(x.s.lq - rr) * H * 4), sb + Sh::OFF_RS + jj * 256, voff);
         }
       }
     }
     if constexpr (BIAS) {
       // query rows t*QS .., keys kt*KT .. of the bias block; the offsets follow lk
       if (t == 0) bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
       const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
-      bload.issue(sb + Sh::OFF_B, rsrc_at(x.rb, off, x.brec - off), wave);
+      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(A_bias) + e0, 0);
+      // query rows past the sample end read as zero, like their Q, dO and
+      // row statistics: their P is then finite and their dS exactly zero
+      bload.issue_rows(sb + Sh::OFF_B, rsrc_at(rb, off, (A_bias_elems - e0) * 2 - off), wave, lane, x.s.lq - r0);
     }
   };
 
@@ -190,41 +215,64 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   int pu = u_begin, pt = 0, pst = 0;
   Unit pinfo;
   if (pu < u_end) pinfo = fetch(pu);
-  auto produce = [&]() -> bool {
+  // Vector memory operations this wave has issued, and the count right after
+  // the loads of the step held by each stage.
+  constexpr int S_OPS = DBIAS != 0 ? 16 : 0;  // dBias stores per step
+  const int step_ops = 2 * loads_of(Sh::QNI, wave, NW) + loads_of(Sh::NRS, wave, NW) + loads_of(Sh::BNI, wave, NW);
+  // produce() runs once before each acquisition (after NS - 2 initial
+  // calls), so the step being acquired was issued by the (NS - 2)-th latest
+  // call: m1 / m2 hold the counts after the latest two calls.
+  int issued = 0, m1 = 0, m2 = 0;
+  auto produce = [&]() __attribute__((always_inline)) {
     while (pu < u_end && pt >= pinfo.n) {
       ++pu;
       pt = 0;
       if (pu < u_end) pinfo = fetch(pu);
     }
-    if (pu >= u_end) return false;
-    issue_step(pinfo, pt, pst);
-    ++pt;
-    pst = pst + 1 == NS ? 0 : pst + 1;
-    return true;
+    if (pu < u_end) {
+      issue_step(pinfo, pt, pst);
+      issued += step_ops;
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+    }
+    m2 = m1;
+    m1 = issued;
+  };
+  // wait until the loads of the step being acquired have landed: everything
+  // issued after them may stay in flight (the K/V loads, which this count
+  // leaves out, only make the wait stricter)
+  auto acquire = [&]() __attribute__((always_inline)) {
+    const int after = issued - (NS == 4 ? m2 : m1);
+    wait_vmcnt_le<0, 63>(max(min(after, 63), 0));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // K and V fragments (MFMA B operand) of this lane's key row
-  auto load_kv = [&](const Unit& x, bf16x8* kf, bf16x8* vf) {
+  // K and V fragments (MFMA B operand) of this lane's key row.  Loaded with
+  // loads the compiler sees, so that it waits for them before any use or
+  // register copy (an asm load's outputs count as ready at once).
+  bf16x8 kf[NKK], vf[NKK];
+  auto load_kv = [&](const Unit& x) __attribute__((always_inline)) {
     const int64_t ko = ((int64_t)x.s.k0 * H + x.h) * D;
-    const uint32_t rec = (uint32_t)x.s.lk * HD * 2;
-    const i32x4 rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + ko, rec);
-    const i32x4 rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + ko, rec);
+    const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(A_k) + ko, (uint32_t)x.s.lk * HD * 2);
+    const rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(A_v) + ko, (uint32_t)x.s.lk * HD * 2);
     const int key = x.kt * KT + wv * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint32_t voff = (uint32_t)(key * HD + kk * 16 + g * 8) * 2;
-      asm_load16(kf[kk], rk, voff);
-      asm_load16(vf[kk], rv, voff);
+      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, voff));
+      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, voff));
     }
   };
 
   // ---- epilogue: dK = scale * dK^T^T, dV (key-split partials summed) ----
-  auto store_unit = [&](const Unit& x, f32x16* dkacc, f32x16* dvacc, int last_stage) {
+  auto store_unit = [&](const Unit& x, f32x16* dkacc, f32x16* dvacc, int last_stage) __attribute__((always_inline)) {
     float* comb = reinterpret_cast<float*>(smem + last_stage * Sh::STAGE);
     const int key = x.kt * KT + wv * 32 + l32;
     const int64_t ko = ((int64_t)x.s.k0 * H + x.h) * D;
-    TG* dkrow = reinterpret_cast<TG*>(a.dk) + ko + (int64_t)key * HD;
-    TG* dvrow = reinterpret_cast<TG*>(a.dv) + ko + (int64_t)key * HD;
+    TG* dkrow = reinterpret_cast<TG*>(A_dk) + ko + (int64_t)key * HD;
+    TG* dvrow = reinterpret_cast<TG*>(A_dv) + ko + (int64_t)key * HD;
     const bool valid = key < x.s.lk;
     if (WKQ > 1 && x.n > 0) {
       // partial of query block wq at [slot][d][key]; lane-dependent part in one base
@@ -259,42 +307,41 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int col = d * 32 + i4 * 8 + g * 4;
-          store4<TG>(dkrow + col, dkacc[d][i4 * 4] * a.scale, dkacc[d][i4 * 4 + 1] * a.scale,
-                     dkacc[d][i4 * 4 + 2] * a.scale, dkacc[d][i4 * 4 + 3] * a.scale);
+          store4<TG>(dkrow + col, dkacc[d][i4 * 4] * A_scale, dkacc[d][i4 * 4 + 1] * A_scale,
+                     dkacc[d][i4 * 4 + 2] * A_scale, dkacc[d][i4 * 4 + 3] * A_scale);
           store4<TG>(dvrow + col, dvacc[d][i4 * 4], dvacc[d][i4 * 4 + 1], dvacc[d][i4 * 4 + 2],
                      dvacc[d][i4 * 4 + 3]);
         }
     }
   };
 
-  // ---- one step of compute on stage st ----
-  auto compute_step = [&](const Unit& x, int t, int st, bf16x8* kf, bf16x8* vf, f32x16* dkacc, f32x16* dvacc,
-                          auto&& after_sdp) {
+  // ---- phase 1: S = Q K^T and dP = dO V^T of the step in stage st ----
+  struct SD {
+    f32x16 s, dp;
+  };
+  auto sdp = [&](int st) __attribute__((always_inline)) {
     const char* qt = smem + st * Sh::STAGE;
     const char* ot = qt + Sh::OFF_O;
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    bf16x8 qa[NKK], oa[NKK];
+    SD r;
+    r.s = f32x16{};
+    r.dp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      qa[kk] = rows_frag<D, PAD>(qt, wq * 32 + l32, kk, g);
-      oa[kk] = rows_frag<D, PAD>(ot, wq * 32 + l32, kk, g);
+      r.s = Elem<bf16>::mma(rows_frag<D, PAD>(qt, wq * 32 + l32, kk, g), kf[kk], r.s);
+      r.dp = Elem<bf16>::mma(rows_frag<D, PAD>(ot, wq * 32 + l32, kk, g), vf[kk], r.dp);
     }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      sacc = Elem<bf16>::mma(qa[kk], kf[kk], sacc);
-      dpacc = Elem<bf16>::mma(oa[kk], vf[kk], dpacc);
-    }
-    // keep several fragment reads in flight ahead of the MFMA chain
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int kk = 0; kk < NKK - 3; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-    after_sdp();  // K/V fragments are dead from here on in the last step of a unit
+    return r;
+  };
+
+  // ---- phase 2: P, dS (bf16 MFMA operands) and dBias of step t (stage st) ----
+  struct Ops {
+    bf16x8 ph[2], dh[2], pl[2], dl[2];
+  };
+  auto softmax = [&](const Unit& x, int t, int st, const SD& sd) __attribute__((always_inline)) {
+    const f32x16 sacc = sd.s, dpacc = sd.dp;
+    Ops o;
+    const char* qt = smem + st * Sh::STAGE;
     float p[16], ds[16];
-    const bool last_step = t + 1 == x.n;
     if constexpr (BIAS) {
       // bias[q][key] for the 16 query rows of this lane (keys past lk carry
       // the next row's values; only their own, unstored columns see them)
@@ -302,16 +349,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         p[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(bt + acc_row(i, 0) * Sh::BT::PITCH) << 16);
-      if (last_step && x.tail) {
-        // the tensor's last element may straddle the end of the bias range by
-        // half a dword, which the range check drops: reload it
-        const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(a.bias) + (a.bias_elems - 1), 2);
-        const float last = __uint_as_float((uint32_t)buf_load2(rl, 0) << 16);
-        const int key = x.kt * KT + wv * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          p[i] = (key == x.s.lk - 1 && t * QS + wq * 32 + acc_row(i, g) == x.s.lq - 1) ? last : p[i];
-      }
     }
     if constexpr (SOFTMAX) {
       const char* rs = qt + Sh::OFF_RS;
@@ -326,34 +363,23 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int j = 0; j < 4; ++j) {
           const int i = i4 * 4 + j;
           const float c = BIAS ? fmaf(p[i], kLog2e, -l4[j]) : -l4[j];
-          p[i] = fast_exp2(fmaf(sacc[i], a.scale_log2, c));
+          p[i] = fast_exp2(fmaf(sacc[i], A_scale_log2, c));
           ds[i] = p[i] * (dpacc[i] - d4[j]);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float xv = BIAS ? fmaf(sacc[i], a.scale, p[i]) : sacc[i] * a.scale;
+        const float xv = BIAS ? fmaf(sacc[i], A_scale, p[i]) : sacc[i] * A_scale;
         p[i] = act_fwd(ACT, xv);
         ds[i] = act_grad(ACT, xv) * dpacc[i];
-      }
-    }
-    if (last_step) {
-      // query rows past the sample end: zero Q, dO and row statistics make
-      // their terms vanish unless the bias of another row overflowed P
-      const int qrem = x.s.lq - (t * QS + wq * 32);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = acc_row(i, g) < qrem;
-        p[i] = ok ? p[i] : 0.0f;
-        ds[i] = ok ? ds[i] : 0.0f;
       }
     }
     if constexpr (DBIAS != 0) {
       // dBias[q][key] = dS; rows past the sample end fall outside the
       // descriptor, and a lane whose key is past the end stores out of range
       const int key = x.kt * KT + wv * 32 + l32;
-      const rsrc_t rdbr = make_rsrc(reinterpret_cast<const char*>(a.dbias) +
+      const rsrc_t rdbr = make_rsrc(reinterpret_cast<const char*>(A_dbias) +
                                         (x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk) * ESB,
                                     (uint32_t)x.s.lq * x.s.lk * ESB);
       const uint32_t vb = key < x.s.lk ? (uint32_t)(((t * QS + wq * 32 + g * 4) * x.s.lk + key) * ESB)
@@ -366,74 +392,176 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)ds[i]), rdbr, voff, 0, 0);
       }
+      issued += S_OPS;
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 ph = pack8(&p[s2 * 8]), dh = pack8(&ds[s2 * 8]);
-      bf16x8 pl, dl;
+      o.ph[s2] = pack8(&p[s2 * 8]);
+      o.dh[s2] = pack8(&ds[s2 * 8]);
       if constexpr (SPLIT) {
         float r1[8], r2[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          r1[j] = p[s2 * 8 + j] - (float)ph[j];
-          r2[j] = ds[s2 * 8 + j] - (float)dh[j];
+          r1[j] = p[s2 * 8 + j] - (float)o.ph[s2][j];
+          r2[j] = ds[s2 * 8 + j] - (float)o.dh[s2][j];
         }
-        pl = pack8(r1);
-        dl = pack8(r2);
+        o.pl[s2] = pack8(r1);
+        o.dl[s2] = pack8(r2);
       }
+    }
+    return o;
+  };
+
+  // ---- phase 3: dV^T += dO^T P, dK^T += Q^T dS from stage st ----
+  auto dkdv_mma = [&](int st, const Ops& o, f32x16* dkacc, f32x16* dvacc) __attribute__((always_inline)) {
+    const char* qt = smem + st * Sh::STAGE;
+    const char* ot = qt + Sh::OFF_O;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const bf16x8 oa = trans_frag<D, PAD>(ot, wq, s2, d * 32, lane);
         const bf16x8 qa = trans_frag<D, PAD>(qt, wq, s2, d * 32, lane);
-        dvacc[d] = Elem<bf16>::mma(oa, ph, dvacc[d]);
-        dkacc[d] = Elem<bf16>::mma(qa, dh, dkacc[d]);
+        dvacc[d] = Elem<bf16>::mma(oa, o.ph[s2], dvacc[d]);
+        dkacc[d] = Elem<bf16>::mma(qa, o.dh[s2], dkacc[d]);
         if constexpr (SPLIT) {
-          dvacc[d] = Elem<bf16>::mma(oa, pl, dvacc[d]);
-          dkacc[d] = Elem<bf16>::mma(qa, dl, dkacc[d]);
+          dvacc[d] = Elem<bf16>::mma(oa, o.pl[s2], dvacc[d]);
+          dkacc[d] = Elem<bf16>::mma(qa, o.dl[s2], dkacc[d]);
         }
       }
     }
   };
 
-  // Wait for the loads of the step about to be computed (and, at a unit
-  // boundary, the K/V loads issued in the previous step).  Vector memory
-  // operations complete in issue order, so every operation issued after the
-  // needed ones may stay in flight: the previous step's prefetch (`recent`)
-  // and the dBias stores of the last two steps (S per step, issued after
-  // each step's prefetch; the older batch only when no K/V load sits between).
-  auto wait_step = [&](bool boundary, int computed, int recent) {
-    if constexpr (NS == 3) {
-      constexpr int S = DBIAS != 0 ? 16 : 0;
-      static_assert(2 * S + L < 64, "vmcnt range");
-      const int ns = (computed >= 1 ? 1 : 0) + ((computed >= 2 && !boundary) ? 1 : 0);
-      if (recent > 0) {
-        if (ns == 2) wait_vmcnt<2 * S + L>();
-        else if (ns == 1) wait_vmcnt<S + L>();
-        else wait_vmcnt<L>();
-      } else {
-        if (ns == 2) wait_vmcnt<2 * S>();
-        else if (ns == 1) wait_vmcnt<S>();
-        else wait_vmcnt<0>();
+  // ---- phases 1 + 2 fused: S/dP of the step in stage cn, written out so
+  // that each of its 16 MFMAs is followed by the VALU work of one element of
+  // P/dS (and its dBias store) of step t in stage cs; a scheduling fence
+  // after each pair keeps that order, so the matrix core and the VALU work
+  // side by side.  Operand LDS reads run two MFMAs ahead.
+  auto sdp_softmax = [&](int cn, const Unit& x, int t, int cs_, const SD& cur, SD& nx,
+                         Ops& o) __attribute__((always_inline)) {
+    const char* qn = smem + cn * Sh::STAGE;
+    const char* on = qn + Sh::OFF_O;
+    const char* qt = smem + cs_ * Sh::STAGE;
+    float bias[16], lse[16], di[16];
+    if constexpr (BIAS) {
+      const char* bt = qt + Sh::OFF_B + (wq * 32 + g * 4) * Sh::BT::PITCH + (wv * 32 + l32) * 2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        bias[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(bt + acc_row(i, 0) * Sh::BT::PITCH) << 16);
+    }
+    if constexpr (SOFTMAX) {
+      const char* rs = qt + Sh::OFF_RS;
+      constexpr int DI_OFF = (Sh::NRS / 2) * 256;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r = wq * 32 + i4 * 8 + g * 4;
+        const int jl = r / 64, rl = r % 64;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rs + jl * 256 + rl * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(rs + DI_OFF + jl * 256 + rl * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lse[i4 * 4 + j] = l4[j];
+          di[i4 * 4 + j] = d4[j];
+        }
       }
-    } else {
-      wait_vmcnt<0>();
+    }
+    // dBias[q][key] = dS; rows past the sample end fall outside the
+    // descriptor, and a lane whose key is past the end stores out of range
+    uint32_t vb = 0;
+    if constexpr (DBIAS != 0) {
+      const int key = x.kt * KT + wv * 32 + l32;
+      vb = key < x.s.lk ? (uint32_t)(((t * QS + wq * 32 + g * 4) * x.s.lk + key) * ESB) : 0x80000000u;
+    }
+    bf16x8 qa[NKK], oa[NKK];
+    qa[0] = rows_frag<D, PAD>(qn, wq * 32 + l32, 0, g);
+    oa[0] = rows_frag<D, PAD>(on, wq * 32 + l32, 0, g);
+    if constexpr (NKK > 1) {
+      qa[1] = rows_frag<D, PAD>(qn, wq * 32 + l32, 1, g);
+      oa[1] = rows_frag<D, PAD>(on, wq * 32 + l32, 1, g);
+    }
+    nx.s = f32x16{};
+    nx.dp = f32x16{};
+    float p[16], ds[16];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int kk = c / 2 % NKK;
+      if (c < 2 * NKK) {
+        if (c % 2 == 0) {
+          nx.s = Elem<bf16>::mma(qa[kk], kf[kk], nx.s);
+          if (kk + 2 < NKK) qa[kk + 2] = rows_frag<D, PAD>(qn, wq * 32 + l32, kk + 2, g);
+        } else {
+          nx.dp = Elem<bf16>::mma(oa[kk], vf[kk], nx.dp);
+          if (kk + 2 < NKK) oa[kk + 2] = rows_frag<D, PAD>(on, wq * 32 + l32, kk + 2, g);
+        }
+      }
+      // element c of P and dS of step t
+      const float sv = cur.s[c], dpv = cur.dp[c];
+      if constexpr (SOFTMAX) {
+        const float cc = BIAS ? fmaf(bias[c], kLog2e, -lse[c]) : -lse[c];
+        p[c] = fast_exp2(fmaf(sv, A_scale_log2, cc));
+        ds[c] = p[c] * (dpv - di[c]);
+      } else {
+        const float xv = BIAS ? fmaf(sv, A_scale, bias[c]) : sv * A_scale;
+        p[c] = act_fwd(ACT, xv);
+        ds[c] = act_grad(ACT, xv) * dpv;
+      }
+      if constexpr (DBIAS != 0) {
+        const rsrc_t rdbr = make_rsrc(
+            reinterpret_cast<const char*>(A_dbias) + (x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk) * ESB,
+            (uint32_t)x.s.lq * x.s.lk * ESB);
+        const uint32_t voff = vb + (uint32_t)(((c >> 2) * 8 + (c & 3)) * x.s.lk * ESB);
+        if constexpr (DBIAS == 2)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ds[c]), rdbr, voff, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)ds[c]), rdbr, voff, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DBIAS != 0) issued += S_OPS;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      o.ph[s2] = pack8(&p[s2 * 8]);
+      o.dh[s2] = pack8(&ds[s2 * 8]);
+      if constexpr (SPLIT) {
+        float r1[8], r2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          r1[j] = p[s2 * 8 + j] - (float)o.ph[s2][j];
+          r2[j] = ds[s2 * 8 + j] - (float)o.dh[s2][j];
+        }
+        o.pl[s2] = pack8(r1);
+        o.dl[s2] = pack8(r2);
+      }
+    }
+  };
+
+  // The bias tensor's last element may straddle the end of its range by half
+  // a dword, which the range check drops.  In the step that holds it (the
+  // last step of the last key tile of the tensor's last (sample, head)),
+  // one lane writes it into the bias tile after the tile has landed; a
+  // second barrier publishes it.  Called after every acquisition, outside
+  // the branch-free compute region.
+  auto patch_tail = [&](const Unit& x, int t, int st) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      if (t + 1 == x.n && x.s.bias0 + (int64_t)(x.h + 1) * x.s.lq * x.s.lk == A_bias_elems &&
+          (x.s.lk - 1) / KT == x.kt) {
+        if (wave == 0 && lane == 0) {
+          const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(A_bias) + (A_bias_elems - 1), 2);
+          const uint16_t last = buf_load2(rl, 0);
+          char* bt = smem + st * Sh::STAGE + Sh::OFF_B;
+          *reinterpret_cast<uint16_t*>(bt + ((x.s.lq - 1) - t * QS) * Sh::BT::PITCH + ((x.s.lk - 1) - x.kt * KT) * 2) = last;
+        }
+        __syncthreads();
+      }
     }
   };
 
   // ---- consumer ----
   if (u_begin >= u_end) return;
-  bf16x8 kf[NKK], vf[NKK];
-  int cs = 0;        // stage of the next step to compute
-  int recent = 0;    // did the previous iteration issue a step (NS == 3)
-  int computed = 0;  // steps computed so far
-  {
-    int u0 = u_begin;
-    Unit x0 = fetch(u0);
-    while (x0.n == 0 && u0 + 1 < u_end) x0 = fetch(++u0);
-    if (x0.n > 0) load_kv(x0, kf, vf);
-  }
-  for (int j = 0; j < NS - 1; ++j) recent = produce() ? 1 : 0;
+  for (int j = 0; j < NS - 2; ++j) produce();
 
+  int cs = 0;  // stage of the step whose P/dS is computed next
   for (int u = u_begin; u < u_end; ++u) {
     const Unit x = fetch(u);
     f32x16 dkacc[ND], dvacc[ND];
@@ -443,36 +571,30 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       dvacc[d] = f32x16{};
     }
     if (x.n > 0) {
-      // next unit with steps: its K/V replace this unit's in the last step,
-      // right after their last use and before the step's prefetch, so the
-      // next iteration's wait (which leaves only that prefetch in flight)
-      // covers them
-      int un = u + 1;
-      Unit xn = x;
-      bool has_next = false;
-      while (un < u_end) {
-        xn = fetch(un);
-        if (xn.n > 0) {
-          has_next = true;
-          break;
-        }
-        ++un;
+      // this unit's K/V: their latency overlaps the wait for its first step
+      load_kv(x);
+      // prologue: S/dP of step 0
+      acquire();
+      produce();
+      patch_tail(x, 0, cs);
+      SD cur = sdp(cs);
+      for (int t = 0; t + 1 < x.n; ++t) {
+        // S/dP of step t+1 (stage cn) beside P/dS of step t (stage cs)
+        const int cn = cs + 1 == NS ? 0 : cs + 1;
+        acquire();
+        produce();
+        patch_tail(x, t + 1, cn);
+        SD nxt;
+        Ops ops;
+        sdp_softmax(cn, x, t, cs, cur, nxt, ops);
+        dkdv_mma(cs, ops, dkacc, dvacc);
+        cur = nxt;
+        cs = cn;
       }
-      for (int t = 0; t < x.n; ++t) {
-        wait_step(t == 0 && computed > 0, computed, recent);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        const bool last = t + 1 == x.n;
-        compute_step(x, t, cs, kf, vf, dkacc, dvacc, [&]() {
-          if (last && has_next) load_kv(xn, kf, vf);
-          recent = produce() ? 1 : 0;
-        });
-        cs = cs + 1 == NS ? 0 : cs + 1;
-        ++computed;
-      }
+      dkdv_mma(cs, softmax(x, x.n - 1, cs, cur), dkacc, dvacc);
     }
-    store_unit(x, dkacc, dvacc, cs == 0 ? NS - 1 : cs - 1);
+    store_unit(x, dkacc, dvacc, cs);
+    if (x.n > 0) cs = cs + 1 == NS ? 0 : cs + 1;
   }
 }
 

@@ -20,10 +20,7 @@ hipError_t dkdv2_one(const BwdArgs& a, int grid, hipStream_t st) {
 
 template <int D, int WKV, int WKQ, int ACT, bool SPLIT>
 hipError_t dkdv2_bias(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
-  if constexpr (D == 128 && WKQ == 4) {
-    // 128 queries per step leave no room for a bias tile at this head dim
-    if (k.bias) return hipErrorInvalidValue;
-  } else if (k.bias) {
+  if (k.bias) {
     if (k.dbias && k.dbias_f32) return dkdv2_one<D, WKV, WKQ, ACT, true, 2, SPLIT>(a, grid, st);
     if (k.dbias) return dkdv2_one<D, WKV, WKQ, ACT, true, 1, SPLIT>(a, grid, st);
     return dkdv2_one<D, WKV, WKQ, ACT, true, 0, SPLIT>(a, grid, st);
@@ -52,7 +49,13 @@ hipError_t dkdv2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream
 hipError_t JATTN_DKDV2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.wkv == 4) return dkdv2_shape<J_D, 4, 1>(a, k, grid, st);
   if (k.wkv == 2) return dkdv2_shape<J_D, 2, 2>(a, k, grid, st);
-  return dkdv2_shape<J_D, 1, 4>(a, k, grid, st);
+  if constexpr (J_D == 128) {
+    // 128-query steps need 73 KB stages at this head dim: fewer than the
+    // three the pipeline needs fit in LDS; the planner never selects them
+    return hipErrorInvalidValue;
+  } else {
+    return dkdv2_shape<J_D, 1, 4>(a, k, grid, st);
+  }
 }
 
 }  // namespace jattn

@@ -136,6 +136,15 @@ struct BiasLoader {
       if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, voff[j]);
     }
   }
+  // Same, with tile rows at or past `rows` read as zero.
+  __device__ __forceinline__ void issue_rows(uint32_t tile, const i32x4& r, int part, int lane, int rows) const {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int inst = part + j * NPARTS;
+      const int rr = (inst * 64 + lane) / T::SPR;
+      if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, rr < rows ? voff[j] : 0x80000000u);
+    }
+  }
 };
 
 // Eight consecutive bf16 (one aligned 16-byte LDS read) widened to fp32.
