@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (1 = headline)")
-    ap.add_argument("--order", default="heavy_first")
+    ap.add_argument("--order", default="zigzag", help="unit order across workers (the zigzag deal by default)")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-mib", type=int, default=1024, help="copy size of the counter calibration")

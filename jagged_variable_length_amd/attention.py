@@ -33,7 +33,7 @@ class JaggedAttention:
                  block_diagonal: bool = False, has_bias: bool = False, want_dbias: bool = False,
                  in_dtype: str = "bf16", out_dtype: Optional[str] = None,
                  grad_dtype: Optional[str] = None, split_operands: bool = False,
-                 order: str = "heavy_first", num_workers: int = 0, scale: Optional[float] = None,
+                 order: str = "zigzag", num_workers: int = 0, scale: Optional[float] = None,
                  dbias_dtype: Optional[str] = None, device="cuda"):
         q_offsets = np.asarray(q_offsets, dtype=np.int64)
         kv_offsets = np.asarray(kv_offsets, dtype=np.int64)

@@ -177,66 +177,96 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     return x;
   };
 
-  // ---- producer: HBM -> LDS loads of one step into one stage ----
-  auto issue_step = [&](const Unit& x, int t, int st) __attribute__((always_inline)) {
-    const uint32_t sb = smem_lds + st * Sh::STAGE;
-    const int r0 = t * QS;
-    const int64_t rec = (int64_t)(x.s.lq - r0) * HD * 2;
-    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D;  // first row of the step
-    qload.issue(sb, rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_q) + qo, 0), 0, rec), wave);
-    qload.issue(sb + Sh::OFF_O, rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_dout) + qo, 0), 0, rec), wave);
-    if constexpr (SOFTMAX) {
-      // load j: rows 64*(j % (NRS/2)) .. of LSE (j < NRS/2) or Di
-      constexpr int HALF = Sh::NRS / 2;
-#pragma unroll
-      for (int j = 0; j < Sh::NRS; j += NW) {
-        const int jj = j + wave;
-        if (jj < Sh::NRS) {
-          const int rr = r0 + 64 * (jj % HALF);
-          const float* rs = (jj < HALF ? A_lse2 : A_di) + ((int64_t)(x.s.q0 + rr) * H + x.h);
-          const uint32_t voff = 64 * (jj % HALF) + lane < QS ? rs_voff : 0x80000000u;
-          lds_dma4(rsrc_at(rsrc_words(rs, 0), 0, (int64_t)(x.s.lq - rr) * H * 4), sb + Sh::OFF_RS + jj * 256, voff);
-        }
-      }
-    }
-    if constexpr (BIAS) {
-      // query rows t*QS .., keys kt*KT .. of the bias block; the offsets follow lk
-      if (t == 0) bload.init(wave, lane, x.s.lk);
-      const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
-      const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
-      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(A_bias) + e0, 0);
-      // query rows past the sample end read as zero, like their Q, dO and
-      // row statistics: their P is then finite and their dS exactly zero
-      bload.issue_rows(sb + Sh::OFF_B, rsrc_at(rb, off, (A_bias_elems - e0) * 2 - off), wave, lane, x.s.lq - r0);
-    }
-  };
-
-  // producer cursor: next (unit, step) to issue; units without steps are skipped
+  // ---- producer: the loads of one step into one stage ----
+  // producer cursor: next (unit, step) to load; units without steps are skipped
   int pu = u_begin, pt = 0, pst = 0;
   Unit pinfo;
   if (pu < u_end) pinfo = fetch(pu);
-  // Vector memory operations this wave has issued, and the count right after
-  // the loads of the step held by each stage.
+  // prepare() advances the cursor and builds the descriptors of the next
+  // step; produce() issues its loads (issue_slot, one per load).  With no
+  // step left, the descriptors have no records and the loads write zeros
+  // into a stage nobody reads.
+  struct StepDMA {
+    uint32_t sb;    // LDS byte address of the stage
+    i32x4 rq, rdo;  // Q, dO rows of the step
+    i32x4 rs;       // this wave's row-stat load (LSE*log2e or Di)
+    i32x4 rb;       // bias rows of the step
+    int brows;      // bias rows inside the sample
+  };
+  constexpr int NJQ = decltype(qload)::NJ, NJB = BIAS ? decltype(bload)::NJ : 0;
+  constexpr int NSLOT = 2 * NJQ + (SOFTMAX ? 1 : 0) + NJB;
+  static_assert(Sh::NRS <= NW, "one row-stat load per wave at most");
   constexpr int S_OPS = DBIAS != 0 ? 16 : 0;  // dBias stores per step
+  // vector memory operations this wave issues per step
   const int step_ops = 2 * loads_of(Sh::QNI, wave, NW) + loads_of(Sh::NRS, wave, NW) + loads_of(Sh::BNI, wave, NW);
-  // produce() runs once before each acquisition (after NS - 2 initial
-  // calls), so the step being acquired was issued by the (NS - 2)-th latest
-  // call: m1 / m2 hold the counts after the latest two calls.
+  // Vector memory operations this wave has issued, and marks after the
+  // loads of the two most recently produced steps: produce() runs once per
+  // acquisition (after NS - 2 initial calls), so the step being acquired is
+  // the (NS - 2)-th latest.
   int issued = 0, m1 = 0, m2 = 0;
-  auto produce = [&]() __attribute__((always_inline)) {
+  auto prepare = [&]() __attribute__((always_inline)) {
     while (pu < u_end && pt >= pinfo.n) {
       ++pu;
       pt = 0;
       if (pu < u_end) pinfo = fetch(pu);
     }
-    if (pu < u_end) {
-      issue_step(pinfo, pt, pst);
-      issued += step_ops;
+    const bool active = pu < u_end;
+    const Unit& x = pinfo;
+    const int t = pt;
+    StepDMA d;
+    d.sb = smem_lds + pst * Sh::STAGE;
+    const int r0 = t * QS;
+    const int64_t rec = active ? (int64_t)(x.s.lq - r0) * HD * 2 : 0;
+    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D;  // first row of the step
+    d.rq = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_q) + qo, 0), 0, rec);
+    d.rdo = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_dout) + qo, 0), 0, rec);
+    if constexpr (SOFTMAX) {
+      // load `wave`: rows 64*(wave % (NRS/2)) .. of LSE (wave < NRS/2) or Di
+      constexpr int HALF = Sh::NRS / 2;
+      const int jj = wave < Sh::NRS ? wave : 0;
+      const int rr = r0 + 64 * (jj % HALF);
+      const float* rsp = (jj < HALF ? A_lse2 : A_di) + ((int64_t)(x.s.q0 + rr) * H + x.h);
+      d.rs = rsrc_at(rsrc_words(rsp, 0), 0, active ? (int64_t)(x.s.lq - rr) * H * 4 : 0);
+    }
+    if constexpr (BIAS) {
+      // query rows t*QS .., keys kt*KT .. of the bias block; the offsets follow
+      // lk; query rows past the sample end read as zero, like their Q, dO and
+      // row statistics: their P is then finite and their dS exactly zero
+      if (active && t == 0) bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
+      const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
+      d.rb = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_bias) + e0, 0), off,
+                     active ? (A_bias_elems - e0) * 2 - off : 0);
+      d.brows = x.s.lq - r0;
+    }
+    issued += step_ops;
+    m2 = m1;
+    m1 = issued;
+    if (active) {
       ++pt;
       pst = pst + 1 == NS ? 0 : pst + 1;
     }
-    m2 = m1;
-    m1 = issued;
+    return d;
+  };
+  // slot c (a compile-time constant after unrolling) of this wave's loads
+  auto issue_slot = [&](const StepDMA& d, int c) __attribute__((always_inline)) {
+    if (c < NJQ) {
+      qload.issue_one(c, d.sb, d.rq, wave);
+    } else if (c < 2 * NJQ) {
+      qload.issue_one(c - NJQ, d.sb + Sh::OFF_O, d.rdo, wave);
+    } else if (SOFTMAX && c == 2 * NJQ) {
+      if (wave < Sh::NRS) {
+        const uint32_t voff = 64 * (wave % (Sh::NRS / 2)) + lane < QS ? rs_voff : 0x80000000u;
+        lds_dma4(d.rs, d.sb + Sh::OFF_RS + wave * 256, voff);
+      }
+    } else if (BIAS && c < NSLOT) {
+      bload.issue_one_rows(c - 2 * NJQ - (SOFTMAX ? 1 : 0), d.sb + Sh::OFF_B, d.rb, wave, lane, d.brows);
+    }
+  };
+  auto produce = [&]() __attribute__((always_inline)) {
+    const StepDMA d = prepare();
+#pragma unroll
+    for (int c = 0; c < NSLOT; ++c) issue_slot(d, c);
   };
   // wait until the loads of the step being acquired have landed: everything
   // issued after them may stay in flight (the K/V loads, which this count
@@ -249,10 +279,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // K and V fragments (MFMA B operand) of this lane's key row.  Loaded with
-  // loads the compiler sees, so that it waits for them before any use or
-  // register copy (an asm load's outputs count as ready at once).
-  bf16x8 kf[NKK], vf[NKK];
+  // K and V fragments (MFMA B operand) of this lane's key row, and those of
+  // the next unit with steps (kn, vn), loaded one unit ahead.  Loads the
+  // compiler sees: it waits for them before any use or register copy (an
+  // asm load's outputs would count as ready at once).
+  bf16x8 kf[NKK], vf[NKK], kn[NKK], vn[NKK];
   auto load_kv = [&](const Unit& x) __attribute__((always_inline)) {
     const int64_t ko = ((int64_t)x.s.k0 * H + x.h) * D;
     const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(A_k) + ko, (uint32_t)x.s.lk * HD * 2);
@@ -261,8 +292,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint32_t voff = (uint32_t)(key * HD + kk * 16 + g * 8) * 2;
-      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, voff));
-      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, voff));
+      kn[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, voff));
+      vn[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, voff));
     }
   };
 
@@ -495,6 +526,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           if (kk + 2 < NKK) oa[kk + 2] = rows_frag<D, PAD>(on, wq * 32 + l32, kk + 2, g);
         }
       }
+
       // element c of P and dS of step t
       const float sv = cur.s[c], dpv = cur.dp[c];
       if constexpr (SOFTMAX) {
@@ -560,6 +592,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // ---- consumer ----
   if (u_begin >= u_end) return;
   for (int j = 0; j < NS - 2; ++j) produce();
+  // first unit with steps: its K/V
+  for (int u0 = u_begin; u0 < u_end; ++u0) {
+    const Unit x0 = fetch(u0);
+    if (x0.n > 0) {
+      load_kv(x0);
+      break;
+    }
+  }
 
   int cs = 0;  // stage of the step whose P/dS is computed next
   for (int u = u_begin; u < u_end; ++u) {
@@ -571,8 +611,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       dvacc[d] = f32x16{};
     }
     if (x.n > 0) {
-      // this unit's K/V: their latency overlaps the wait for its first step
-      load_kv(x);
+      // this unit's K/V (loaded one unit ahead); then the next unit's
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        kf[kk] = kn[kk];
+        vf[kk] = vn[kk];
+      }
+      for (int un = u + 1; un < u_end; ++un) {
+        const Unit xn = fetch(un);
+        if (xn.n > 0) {
+          load_kv(xn);
+          break;
+        }
+      }
       // prologue: S/dP of step 0
       acquire();
       produce();
@@ -596,6 +647,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     store_unit(x, dkacc, dvacc, cs);
     if (x.n > 0) cs = cs + 1 == NS ? 0 : cs + 1;
   }
+  // loads issued past the last step (zero records) must land before the
+  // workgroup's LDS is released
+  wait_vmcnt<0>();
 }
 
 }  // namespace jattn

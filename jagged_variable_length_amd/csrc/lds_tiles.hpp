@@ -100,10 +100,12 @@ struct RowLoader {
   // part must be wave-uniform; tile is the LDS byte address of the tile
   __device__ __forceinline__ void issue(uint32_t tile, const i32x4& r, int part) const {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int inst = part + j * NPARTS;
-      if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, voff[j]);
-    }
+    for (int j = 0; j < NJ; ++j) issue_one(j, tile, r, part);
+  }
+  // the j-th load of this part (j a compile-time constant after unrolling)
+  __device__ __forceinline__ void issue_one(int j, uint32_t tile, const i32x4& r, int part) const {
+    const int inst = part + j * NPARTS;
+    if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, voff[j]);
   }
 };
 
@@ -139,11 +141,13 @@ struct BiasLoader {
   // Same, with tile rows at or past `rows` read as zero.
   __device__ __forceinline__ void issue_rows(uint32_t tile, const i32x4& r, int part, int lane, int rows) const {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int inst = part + j * NPARTS;
-      const int rr = (inst * 64 + lane) / T::SPR;
-      if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, rr < rows ? voff[j] : 0x80000000u);
-    }
+    for (int j = 0; j < NJ; ++j) issue_one_rows(j, tile, r, part, lane, rows);
+  }
+  __device__ __forceinline__ void issue_one_rows(int j, uint32_t tile, const i32x4& r, int part, int lane,
+                                                 int rows) const {
+    const int inst = part + j * NPARTS;
+    const int rr = (inst * 64 + lane) / T::SPR;
+    if (NI % NPARTS == 0 || inst < NI) lds_dma16(r, tile + inst * 1024, rr < rows ? voff[j] : 0x80000000u);
   }
 };
 

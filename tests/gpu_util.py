@@ -20,7 +20,7 @@ def say(*a):
 
 
 def make_op(inp: gen.JaggedInputs, *, act="softmax", block=False, bias=False, want_dbias=False,
-            out_dtype=None, grad_dtype=None, split=False, order="heavy_first", num_workers=0, dbias_dtype=None):
+            out_dtype=None, grad_dtype=None, split=False, order="zigzag", num_workers=0, dbias_dtype=None):
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, inp.H, inp.D, act=act, block_diagonal=block,
                            has_bias=bias, want_dbias=want_dbias, in_dtype=inp.dtype, out_dtype=out_dtype,
                            grad_dtype=grad_dtype, split_operands=split, order=order,
