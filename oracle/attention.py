@@ -18,6 +18,12 @@ jagged batch, one (sample, head) at a time, in float64:
   would be; no normalisation.
 * same post, section "BlockAttention": fixed 64-token blocks; query block i
   sees only key/value block i.
+* same post, section "BlockAttention" (its account of the sliding-window
+  kernel that came before block attention): each token attends only to
+  nearby events of its own sequence.  The pages give no window size and no
+  direction, so the window is two parameters (left, right): query i of a
+  sample sees key j iff  i - left <= j <= i + right  (self-attention only,
+  lq == lk per sample).  (left, right) = (inf, 0) is causal attention.
 
 Conventions (readings where the pages are silent):
   S = scale * Q K^T + bias   (bias added after scaling, shape [H, lq, lk])
@@ -92,11 +98,26 @@ def bias_starts(lq, lk, H):
     return start
 
 
-def allowed_mask(lq, lk, block_diagonal):
-    """Allowed (i, j) pairs: all of them, or floor(i/64) == floor(j/64)."""
+def allowed_mask(lq, lk, block_diagonal, window=None):
+    """Allowed (i, j) pairs: all of them, floor(i/64) == floor(j/64), or
+    (sliding window (left, right)) i - left <= j <= i + right."""
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    if window is not None:
+        left, right = window
+        return (j >= i - left) & (j <= i + right)
     if not block_diagonal:
         return np.ones((lq, lk), dtype=bool)
-    return (np.arange(lq)[:, None] // BLOCK) == (np.arange(lk)[None, :] // BLOCK)
+    return (i // BLOCK) == (j // BLOCK)
+
+
+def _check_mask_args(lq, lk, block_diagonal, window):
+    if block_diagonal and window is not None:
+        raise ValueError("block-diagonal and sliding-window masks are exclusive")
+    if (block_diagonal or window is not None) and np.any(lq != lk):
+        raise ValueError("block-diagonal / sliding-window attention needs lq == lk per sample")
+    if window is not None and (window[0] < 0 or window[1] < 0):
+        raise ValueError("window sides must be >= 0")
 
 
 def _scores(Qb, Kb, scale, bias_bh):
@@ -129,7 +150,7 @@ def _probabilities(S, allowed, activation):
 # forward
 # ----------------------------------------------------------------------------
 def forward(q, k, v, q_offsets, kv_offsets, *, scale=None, activation="softmax",
-            block_diagonal=False, bias=None):
+            block_diagonal=False, bias=None, window=None):
     """O [Tq,H,D] and LSE [Tq,H] (None for GDPA activations), all fp64.
 
     q, k, v: float64 [T, H, D]; bias: float64 flat per-sample [H, lq, lk].
@@ -138,8 +159,7 @@ def forward(q, k, v, q_offsets, kv_offsets, *, scale=None, activation="softmax",
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     q0, lq = _lengths(q_offsets)
     k0, lk = _lengths(kv_offsets)
-    if block_diagonal and np.any(lq != lk):
-        raise ValueError("block-diagonal attention needs lq == lk per sample")
+    _check_mask_args(lq, lk, block_diagonal, window)
     bstart = bias_starts(lq, lk, H)
     o = np.zeros((Tq, H, D))
     lse = np.full((Tq, H), -np.inf) if activation == "softmax" else None
@@ -151,7 +171,7 @@ def forward(q, k, v, q_offsets, kv_offsets, *, scale=None, activation="softmax",
         if nk == 0:
             continue  # O = 0, LSE = -inf
         rk = slice(int(k0[b]), int(k0[b]) + nk)
-        allowed = allowed_mask(nq, nk, block_diagonal)
+        allowed = allowed_mask(nq, nk, block_diagonal, window)
         for h in range(H):
             bias_bh = None
             if bias is not None:
@@ -169,7 +189,7 @@ def forward(q, k, v, q_offsets, kv_offsets, *, scale=None, activation="softmax",
 # backward
 # ----------------------------------------------------------------------------
 def backward(q, k, v, dout, q_offsets, kv_offsets, *, scale=None, activation="softmax",
-             block_diagonal=False, bias=None, want_dbias=False):
+             block_diagonal=False, bias=None, want_dbias=False, window=None):
     """dQ, dK, dV (fp64, [T,H,D]) and dBias (flat, or None).
 
     For one (sample, head), with P the forward probabilities/activations:
@@ -183,8 +203,7 @@ def backward(q, k, v, dout, q_offsets, kv_offsets, *, scale=None, activation="so
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     q0, lq = _lengths(q_offsets)
     k0, lk = _lengths(kv_offsets)
-    if block_diagonal and np.any(lq != lk):
-        raise ValueError("block-diagonal attention needs lq == lk per sample")
+    _check_mask_args(lq, lk, block_diagonal, window)
     bstart = bias_starts(lq, lk, H)
     dq = np.zeros((Tq, H, D))
     dk = np.zeros((Tk, H, D))
@@ -196,7 +215,7 @@ def backward(q, k, v, dout, q_offsets, kv_offsets, *, scale=None, activation="so
             continue
         rq = slice(int(q0[b]), int(q0[b]) + nq)
         rk = slice(int(k0[b]), int(k0[b]) + nk)
-        allowed = allowed_mask(nq, nk, block_diagonal)
+        allowed = allowed_mask(nq, nk, block_diagonal, window)
         for h in range(H):
             s0 = int(bstart[b]) + h * nq * nk
             bias_bh = None
@@ -227,21 +246,22 @@ def backward(q, k, v, dout, q_offsets, kv_offsets, *, scale=None, activation="so
 # full workload sizes, where the whole batch would be slow)
 # ----------------------------------------------------------------------------
 def forward_sample(q, k, v, q_offsets, kv_offsets, b, *, scale=None, activation="softmax",
-                   block_diagonal=False, bias=None):
+                   block_diagonal=False, bias=None, window=None):
     """Forward restricted to sample ``b``: returns (O_b [lq,H,D], LSE_b or None)."""
     sub = _sub_batch(q, k, v, None, q_offsets, kv_offsets, b, bias)
     o, lse = forward(sub["q"], sub["k"], sub["v"], sub["qo"], sub["ko"], scale=scale,
-                     activation=activation, block_diagonal=block_diagonal, bias=sub["bias"])
+                     activation=activation, block_diagonal=block_diagonal, bias=sub["bias"],
+                     window=window)
     return o, lse
 
 
 def backward_sample(q, k, v, dout, q_offsets, kv_offsets, b, *, scale=None, activation="softmax",
-                    block_diagonal=False, bias=None, want_dbias=False):
+                    block_diagonal=False, bias=None, want_dbias=False, window=None):
     """Backward restricted to sample ``b``: dQ_b, dK_b, dV_b, dBias_b."""
     sub = _sub_batch(q, k, v, dout, q_offsets, kv_offsets, b, bias)
     return backward(sub["q"], sub["k"], sub["v"], sub["do"], sub["qo"], sub["ko"], scale=scale,
                     activation=activation, block_diagonal=block_diagonal, bias=sub["bias"],
-                    want_dbias=want_dbias)
+                    want_dbias=want_dbias, window=window)
 
 
 def _sub_batch(q, k, v, dout, q_offsets, kv_offsets, b, bias):

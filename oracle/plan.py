@@ -19,6 +19,16 @@ Specification implemented here:
                   cost = ceil(lq_b / step_rows)            (0 when lq_b = 0)
        block    : (b, h, 64-block t) for l_b > 0, cost = 1
      a unit of cost 0 only writes zeros (zero-length partner sample).
+     Sliding window (left, right), lq_b == lk_b ("BlockAttention" section:
+     the sliding-window kernel skips the tiles that lie outside the
+     window): a unit's steps are only those that meet its tile's window.
+       fwd / dq : rows r0..r1 of the tile see keys max(0, r0 - left) ..
+                  min(lk - 1, r1 + right); steps first_key // step_rows ..
+                  last_key // step_rows
+       dkdv     : keys c0..c1 are seen by rows max(0, c0 - right) ..
+                  min(lq - 1, c1 + left), likewise
+     cost = number of those steps.  The first step is not stored: it follows
+     from the tile index and the window.
   2. stable sort by cost, descending (ties stay in (b, h, t) order)
   3. deal to W workers
        heavy_first : sorted position i -> worker i mod W
@@ -46,19 +56,47 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def enumerate_units(kind, lq, lk, H, tile_rows, step_rows, block=64):
+def window_steps(t, tile_rows, step_rows, n_tile, n_step, near, far):
+    """Inner-loop steps (first, count) of tile t of a sliding-window unit.
+
+    The tile covers rows t*tile_rows .. of a sequence of n_tile rows; its
+    partners (n_step of them) range from row - near to row + far."""
+    r0 = t * tile_rows
+    r1 = min(n_tile, r0 + tile_rows) - 1
+    first = max(0, r0 - near)
+    last = min(n_step - 1, r1 + far)
+    if last < first:
+        return first // step_rows, 0
+    return first // step_rows, last // step_rows - first // step_rows + 1
+
+
+def enumerate_units(kind, lq, lk, H, tile_rows, step_rows, block=64, window=None):
     """List of (b, h, t, cost) tuples in (b, h, t) order."""
     units = []
     for b in range(len(lq)):
         nq, nk = int(lq[b]), int(lk[b])
+        if window is not None and kind != KIND_BLOCK and nq != nk:
+            raise ValueError("sliding-window mode needs lq == lk")
         if kind in (KIND_FWD, KIND_DQ):
             if nq == 0:
                 continue
             n_tiles, cost = _ceil_div(nq, tile_rows), _ceil_div(nk, step_rows)
+            if window is not None:
+                for h in range(H):
+                    for t in range(n_tiles):
+                        units.append((b, h, t, window_steps(t, tile_rows, step_rows, nq, nk,
+                                                            window[0], window[1])[1]))
+                continue
         elif kind == KIND_DKDV:
             if nk == 0:
                 continue
             n_tiles, cost = _ceil_div(nk, tile_rows), _ceil_div(nq, step_rows)
+            if window is not None:
+                for h in range(H):
+                    for t in range(n_tiles):
+                        units.append((b, h, t, window_steps(t, tile_rows, step_rows, nk, nq,
+                                                            window[1], window[0])[1]))
+                continue
         elif kind == KIND_BLOCK:
             if nq != nk:
                 raise ValueError("block mode needs lq == lk")
@@ -101,8 +139,8 @@ def deal(units, W, order):
     return ordered, offsets
 
 
-def plan(kind, lq, lk, H, tile_rows, step_rows, W, order, block=64):
-    return deal(enumerate_units(kind, lq, lk, H, tile_rows, step_rows, block), W, order)
+def plan(kind, lq, lk, H, tile_rows, step_rows, W, order, block=64, window=None):
+    return deal(enumerate_units(kind, lq, lk, H, tile_rows, step_rows, block, window), W, order)
 
 
 def worker_loads(ordered, offsets):
