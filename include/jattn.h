@@ -9,12 +9,18 @@
  *   - section "Generalized Dot-Product Attention (GDPA)": the same two
  *     matrix products with GELU or SiLU applied element-wise in place of
  *     softmax (no normalisation);
- *   - section "BlockAttention": a fixed 64-token block-diagonal mask.
+ *   - section "BlockAttention": a fixed 64-token block-diagonal mask, and
+ *     the sliding-window attention that preceded it (each token attends to
+ *     nearby tokens of its own sequence; tiles outside the window are never
+ *     visited).
  * For sample b and head h, with Q_b [lq,D], K_b, V_b [lk,D]:
  *   S = scale * Q_b K_b^T + bias_b[h]
  *   softmax:  P = softmax_row(S), O = P V, LSE_i = ln sum_j exp(S_ij)
  *   GDPA:     P = act(S),        O = P V   (act = erf-GELU or SiLU)
  *   block-diagonal: only pairs with floor(i/64) == floor(j/64) take part.
+ *   sliding window (left, right): only pairs with i - left <= j <= i + right
+ *     take part (self-attention: lq_b == lk_b).  The pages fix no window
+ *     size or direction; (left, right) = (>= max length, 0) is causal.
  * There is no causal mask.  Zero-length samples: rows with lk = 0 get O = 0,
  * LSE = -inf and dQ = 0; rows with lq = 0 get dK = dV = 0.  The library
  * writes these zeros itself and never assumes zeroed output buffers.
@@ -70,6 +76,8 @@ extern "C" {
 /* mask (desc.mask) */
 #define JATTN_MASK_NONE 0
 #define JATTN_MASK_BLOCKDIAG64 1 /* BlockAttention, requires lq_b == lk_b */
+#define JATTN_MASK_WINDOW 2      /* sliding window (window_left, window_right),
+                                    requires lq_b == lk_b and bf16 inputs */
 
 /* element types */
 #define JATTN_BF16 0
@@ -92,7 +100,7 @@ typedef struct {
   int32_t B, H, D;      /* D in {32, 64, 128}; H >= 1; B >= 0 */
   float scale;          /* softmax/GDPA scale; <= 0 selects 1/sqrt(D) */
   int32_t act;          /* JATTN_SOFTMAX | JATTN_GELU_ERF | JATTN_SILU */
-  int32_t mask;         /* JATTN_MASK_NONE | JATTN_MASK_BLOCKDIAG64 */
+  int32_t mask;         /* JATTN_MASK_NONE | JATTN_MASK_BLOCKDIAG64 | JATTN_MASK_WINDOW */
   int32_t has_bias;     /* 0/1: additive bias input */
   int32_t want_dbias;   /* 0/1: backward writes dBias (needs has_bias) */
   int32_t in_dtype;     /* q, k, v, bias, dout: JATTN_BF16 | JATTN_F32 */
@@ -103,6 +111,9 @@ typedef struct {
   int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
   int32_t num_workers;  /* persistent workers per kernel; 0 = default */
   int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
+  int32_t window_left;  /* JATTN_MASK_WINDOW: keys before the query it sees (>= 0) */
+  int32_t window_right; /* JATTN_MASK_WINDOW: keys after the query it sees (>= 0);
+                           both are ignored for other masks */
 } jattn_desc;
 
 /* Per-kernel plan figures.  tile_rows: rows of the unit's own tile (q rows
@@ -135,7 +146,9 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets,
 int jattn_plan_info(const jattn_plan* plan, jattn_plan_summary* summary);
 
 /* Copy a plan part to host memory as int32.  which = JATTN_PLAN_* * 2 + part,
- * part 0 = units as (b, h, tile, cost) quadruples in worker order,
+ * part 0 = units as (b, h, tile, cost) quadruples in worker order (with a
+ * sliding window, cost counts the steps that meet the tile's window; the
+ * first of them follows from the tile index and the window),
  * part 1 = worker offsets [num_workers + 1].  *n receives the number of
  * int32 written (or needed, when dst is NULL).  Host only. */
 int jattn_plan_export(const jattn_plan* plan, int32_t which, int32_t* dst, int64_t cap,
@@ -147,7 +160,7 @@ int jattn_plan_export(const jattn_plan* plan, int32_t which, int32_t* dst, int64
 int jattn_plan_upload(const jattn_plan* plan, void* workspace, int64_t workspace_bytes,
                       void* stream);
 
-/* Forward.  Writes o (out_dtype) and, for softmax with mask NONE, lse.
+/* Forward.  Writes o (out_dtype) and, for softmax with mask NONE or WINDOW, lse.
  * bias: required iff desc.has_bias.  lse may be NULL (not written) for
  * softmax; it must be NULL-or-ignored for GDPA and block mode, which keep
  * no row statistics ("BlockAttention" section: no logsumexp traffic). */
@@ -155,7 +168,7 @@ int jattn_fwd(const jattn_plan* plan, const void* q, const void* k, const void* 
               const void* bias, void* o, float* lse, void* workspace, void* stream);
 
 /* Backward.  Given dout, writes dq, dk, dv (grad_dtype) and, if
- * desc.want_dbias, dbias (dbias_dtype).  Softmax with mask NONE needs o and
+ * desc.want_dbias, dbias (dbias_dtype).  Softmax with mask NONE or WINDOW needs o and
  * the forward's lse (JATTN_E_STATE otherwise); GDPA needs neither; block
  * mode recomputes its row statistics in-tile and needs neither.  Uses the
  * workspace's scratch region for row statistics.  No atomics: every output
@@ -168,7 +181,7 @@ int jattn_bwd(const jattn_plan* plan, const void* q, const void* k, const void* 
 
 /* Backward stages (bit mask for jattn_bwd_stages). */
 #define JATTN_BWD_PREP 1 /* Di = rowsum(dO * O) and LSE * log2(e) into the workspace
-                            (softmax, mask NONE) */
+                            (softmax, mask NONE or WINDOW) */
 #define JATTN_BWD_DKDV 2 /* dK, dV (and dBias) */
 #define JATTN_BWD_DQ 4   /* dQ */
 #define JATTN_BWD_ALL 7

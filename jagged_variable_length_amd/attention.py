@@ -34,7 +34,7 @@ class JaggedAttention:
                  in_dtype: str = "bf16", out_dtype: Optional[str] = None,
                  grad_dtype: Optional[str] = None, split_operands: bool = False,
                  order: str = "zigzag", num_workers: int = 0, scale: Optional[float] = None,
-                 dbias_dtype: Optional[str] = None, device="cuda"):
+                 dbias_dtype: Optional[str] = None, window: Optional[tuple] = None, device="cuda"):
         q_offsets = np.asarray(q_offsets, dtype=np.int64)
         kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
         self.B = len(q_offsets) - 1
@@ -46,12 +46,16 @@ class JaggedAttention:
         self.dbias_dtype = dbias_dtype or self.grad_dtype
         self.has_bias, self.want_dbias = has_bias, want_dbias
         self.block_diagonal = block_diagonal
+        self.window = None if window is None else (int(window[0]), int(window[1]))
         self.scale = (1.0 / math.sqrt(D)) if scale is None else scale
         self.device = torch.device(device)
         d = _b.jattn_desc()
         d.B, d.H, d.D, d.scale = self.B, H, D, self.scale
         d.act = _ACT[act]
         d.mask = _b.JATTN_MASK_BLOCKDIAG64 if block_diagonal else _b.JATTN_MASK_NONE
+        if self.window is not None:
+            d.mask = _b.JATTN_MASK_WINDOW
+            d.window_left, d.window_right = self.window
         d.has_bias, d.want_dbias = int(has_bias), int(want_dbias)
         d.in_dtype, d.out_dtype, d.grad_dtype = _DT[in_dtype], _DT[self.out_dtype], _DT[self.grad_dtype]
         d.split_operands = int(split_operands)

@@ -18,7 +18,7 @@ JATTN_OK = 0
 JATTN_E_NULL, JATTN_E_OFFSETS, JATTN_E_SHAPE, JATTN_E_UNSUPPORTED = -1, -2, -3, -4
 JATTN_E_ALIGN, JATTN_E_WORKSPACE, JATTN_E_STATE, JATTN_E_HIP, JATTN_E_ARG = -5, -6, -7, -8, -9
 JATTN_SOFTMAX, JATTN_GELU_ERF, JATTN_SILU = 0, 1, 2
-JATTN_MASK_NONE, JATTN_MASK_BLOCKDIAG64 = 0, 1
+JATTN_MASK_NONE, JATTN_MASK_BLOCKDIAG64, JATTN_MASK_WINDOW = 0, 1, 2
 JATTN_BF16, JATTN_F32 = 0, 1
 JATTN_HEAVY_FIRST, JATTN_ZIGZAG, JATTN_LPT = 0, 1, 2
 JATTN_PLAN_FWD, JATTN_PLAN_DKDV, JATTN_PLAN_DQ, JATTN_PLAN_BLOCK = 0, 1, 2, 3
@@ -43,7 +43,8 @@ class jattn_desc(ctypes.Structure):
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("split_operands", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("num_workers", ctypes.c_int32),
-                ("dbias_dtype", ctypes.c_int32)]
+                ("dbias_dtype", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 class jattn_kernel_plan(ctypes.Structure):

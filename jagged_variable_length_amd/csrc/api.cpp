@@ -22,6 +22,7 @@ struct jattn_plan {
   int64_t Tq = 0, Tk = 0, bias_elems = 0;
   double pairs = 0.0;  // allowed (i, j) pairs summed over samples (per head)
   int fwd_wq = 4, dq_wq = 4, dkdv_wkv = 4;
+  int win_l = -1, win_r = -1;  // sliding window sides (clamped), -1 without one
   UnitList fwd, dkdv, dq, block;
   std::vector<int32_t> image;  // uploaded plan (int32 words)
   int64_t off_samples = 0, off_fwd_u = 0, off_fwd_o = 0, off_dkdv_u = 0, off_dkdv_o = 0;
@@ -70,6 +71,7 @@ KernelSel base_sel(const jattn_plan* p) {
   k.dbias_f32 = p->desc.dbias_dtype == JATTN_F32;
   k.split = p->desc.split_operands != 0;
   k.in_f32 = p->desc.in_dtype == JATTN_F32;
+  k.window = p->desc.mask == JATTN_MASK_WINDOW;
   return k;
 }
 
@@ -112,8 +114,14 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   if (d.H < 1 || d.H > 4096) return fail(JATTN_E_SHAPE, "H must be in [1, 4096]");
   if (d.D != 32 && d.D != 64 && d.D != 128) return fail(JATTN_E_SHAPE, "D must be 32, 64 or 128");
   if (d.act < JATTN_SOFTMAX || d.act > JATTN_SILU) return fail(JATTN_E_UNSUPPORTED, "unknown activation");
-  if (d.mask != JATTN_MASK_NONE && d.mask != JATTN_MASK_BLOCKDIAG64)
+  if (d.mask != JATTN_MASK_NONE && d.mask != JATTN_MASK_BLOCKDIAG64 && d.mask != JATTN_MASK_WINDOW)
     return fail(JATTN_E_UNSUPPORTED, "unknown mask");
+  if (d.mask == JATTN_MASK_WINDOW) {
+    if (d.window_left < 0 || d.window_right < 0) return fail(JATTN_E_ARG, "window sides must be >= 0");
+    if (d.in_dtype != JATTN_BF16) return fail(JATTN_E_UNSUPPORTED, "sliding-window mode needs bf16 inputs");
+    if (d.want_dbias)
+      return fail(JATTN_E_UNSUPPORTED, "sliding-window mode does not produce dbias (dense [H, lq, lk] layout)");
+  }
   if (d.in_dtype != JATTN_BF16 && d.in_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown in_dtype");
   if (d.out_dtype != JATTN_BF16 && d.out_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown out_dtype");
   if (d.grad_dtype != JATTN_BF16 && d.grad_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown grad_dtype");
@@ -153,6 +161,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
       return fail(JATTN_E_SHAPE, "one sample's dbias block per head must span < 2^30 bytes");
     if (d.mask == JATTN_MASK_BLOCKDIAG64 && a != c)
       return fail(JATTN_E_SHAPE, "block-diagonal mode needs lq == lk for every sample");
+    if (d.mask == JATTN_MASK_WINDOW && a != c)
+      return fail(JATTN_E_SHAPE, "sliding-window mode needs lq == lk for every sample");
     lq[b] = (int32_t)a;
     lk[b] = (int32_t)c;
   }
@@ -166,6 +176,12 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   p->scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.D);
   p->Tq = q_offsets[B];
   p->Tk = kv_offsets[B];
+  if (d.mask == JATTN_MASK_WINDOW) {
+    // a side longer than any sample is unbounded; the clamp keeps the
+    // kernels' row +- side arithmetic inside int32 (rows < 2^25 per sample)
+    p->win_l = std::min(d.window_left, 1 << 30);
+    p->win_r = std::min(d.window_right, 1 << 30);
+  }
 
   // sample table and algorithmic size
   p->image.assign((size_t)8 * B, 0);
@@ -185,6 +201,12 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
         const double r = std::min(64, lq[b] - s0);
         p->pairs += r * r;
       }
+    } else if (d.mask == JATTN_MASK_WINDOW) {
+      // row i sees keys max(0, i - left) .. min(l - 1, i + right)
+      int64_t n = 0;
+      for (int64_t i = 0; i < lq[b]; ++i)
+        n += std::min<int64_t>(lk[b] - 1, i + p->win_r) - std::max<int64_t>(0, i - p->win_l) + 1;
+      p->pairs += (double)n;
     } else {
       p->pairs += (double)lq[b] * (double)lk[b];
     }
@@ -208,6 +230,8 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     p->dq_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
     // nor has the bf16 short-query dQ kernel
     if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias) p->dq_wq = 4;
+    // the windowed kernels exist for 128-row query tiles and 128-key units
+    if (d.mask == JATTN_MASK_WINDOW) p->fwd_wq = p->dq_wq = 4;
     const int fwd_tile = 32 * p->fwd_wq, fwd_step = p->fwd_wq == 4 ? 64 : 128;
     const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
@@ -215,10 +239,14 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     // the bf16 dK/dV kernel keeps three or four step stages in LDS: 128-query
     // steps (32-key units) do not leave room for three at D = 128
     if (d.in_dtype == JATTN_BF16 && d.D == 128 && p->dkdv_wkv == 1) p->dkdv_wkv = 2;
+    if (d.mask == JATTN_MASK_WINDOW) p->dkdv_wkv = 4;
     const int dkdv_tile = 32 * p->dkdv_wkv, dkdv_step = 32 * (4 / p->dkdv_wkv);
-    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd);
-    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq);
-    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, W, order, &p->dkdv);
+    jattn::Window win;
+    win.left = p->win_l;
+    win.right = p->win_r;
+    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd, win);
+    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq, win);
+    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, W, order, &p->dkdv, win);
   }
   append(p->image, p->fwd, &p->off_fwd_u, &p->off_fwd_o);
   append(p->image, p->dkdv, &p->off_dkdv_u, &p->off_dkdv_o);
@@ -318,6 +346,8 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.4426950408889634f;
   a.bias_elems = p->bias_elems;
+  a.win_l = p->win_l;
+  a.win_r = p->win_r;
   KernelSel sel = base_sel(p);
   sel.out_f32 = p->desc.out_dtype == JATTN_F32;
   sel.wq = p->fwd_wq;
@@ -347,7 +377,8 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   if (!p) return fail(JATTN_E_NULL, "null plan");
   if (stages < 0 || stages > JATTN_BWD_ALL) return fail(JATTN_E_ARG, "unknown backward stage mask");
   if (p->Tq == 0 && p->Tk == 0) return ok();
-  const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask == JATTN_MASK_NONE;
+  // softmax outside block mode keeps row statistics from the forward
+  const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask != JATTN_MASK_BLOCKDIAG64;
   if ((p->Tq > 0 && (!q || !dout || !dq)) || (p->Tk > 0 && (!k || !v || !dk || !dv)))
     return fail(JATTN_E_NULL, "null q/k/v/dout/dq/dk/dv");
   if (p->desc.has_bias && !bias && p->bias_elems > 0) return fail(JATTN_E_NULL, "bias required (has_bias = 1)");
@@ -414,6 +445,8 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   a.scale = p->scale;
   a.scale_log2 = p->scale * 1.4426950408889634f;
   a.bias_elems = p->bias_elems;
+  a.win_l = p->win_l;
+  a.win_r = p->win_r;
   if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
     a.units = ws_ptr(workspace, p->off_dkdv_u);
     a.worker_off = ws_ptr(workspace, p->off_dkdv_o);

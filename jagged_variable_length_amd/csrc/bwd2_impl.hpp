@@ -31,6 +31,12 @@
 // loaded right after their last S/dP use.  Vector memory operations complete
 // in issue order, so each wait lets every operation issued after the needed
 // loads stay in flight (exact per-wave counts, dBias stores included).
+//
+// Sliding window (WIN, section "BlockAttention"): a unit's steps start at the
+// first query block whose window reaches its key tile (the plan counts only
+// the steps that meet it); P and dS are zeroed element-wise outside the
+// window, branch-free inside the interleaved loop.  dBias is not produced
+// with a window (its dense [lq, lk] layout would be mostly zeros).
 #pragma once
 #include "common.hpp"
 #include "fwd_impl.hpp"
@@ -119,8 +125,9 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 }
 
 // DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
-template <typename TG, int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT>
+template <typename TG, int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT, bool WIN = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv2_kernel(BwdArgs a) {
+  static_assert(!WIN || DBIAS == 0, "no dBias with a window");
   // Argument fields as locals: the lambdas below capture by reference, and a
   // reference to the argument block itself would keep it in scratch memory.
   const void* const A_q = a.q;
@@ -139,6 +146,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const float A_scale = a.scale;
   const float A_scale_log2 = a.scale_log2;
   const int64_t A_bias_elems = a.bias_elems;
+  const int A_win_l = a.win_l, A_win_r = a.win_r;
   constexpr bool SOFTMAX = (ACT == kSoftmax);
   using Sh = Dkdv2Shape<D, WKV, WKQ, SOFTMAX, BIAS>;
   constexpr int NW = Sh::NW, KT = Sh::KT, QS = Sh::QS, ND = D / 32, NKK = D / 16, NS = Sh::NS;
@@ -175,6 +183,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     x.n = un[3];
     x.s = sload_sample(A_samples, un[0]);
     return x;
+  };
+  // first query row of step t (a windowed unit starts at the first query
+  // block whose window reaches its keys)
+  auto step_row0 = [&](const Unit& x, int t) __attribute__((always_inline)) {
+    return ((WIN ? window_first_step(x.kt * KT, A_win_r, QS) : 0) + t) * QS;
+  };
+  // window test of slot c (query row rbase + acc_row(c, 0)) against this
+  // lane's key, dk = key - rbase: -left <= key - row <= right, row < lq, key < lk
+  auto window_ok = [&](const Unit& x, int dk, int rbase, int key, int c) __attribute__((always_inline)) {
+    const int off = (c >> 2) * 8 + (c & 3);
+    return (uint32_t)(dk - off + A_win_l) <= (uint32_t)(A_win_l + A_win_r) && rbase + off < x.s.lq &&
+           key < x.s.lk;
   };
 
   // ---- producer: the loads of one step into one stage ----
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int t = pt;
     StepDMA d;
     d.sb = smem_lds + pst * Sh::STAGE;
-    const int r0 = t * QS;
+    const int r0 = step_row0(x, t);
     const int64_t rec = active ? (int64_t)(x.s.lq - r0) * HD * 2 : 0;
     const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D;  // first row of the step
     d.rq = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_q) + qo, 0), 0, rec);
@@ -406,6 +426,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         ds[i] = act_grad(ACT, xv) * dpacc[i];
       }
     }
+    if constexpr (WIN) {
+      const int key = x.kt * KT + wv * 32 + l32;
+      const int rbase = step_row0(x, t) + wq * 32 + g * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = window_ok(x, key - rbase, rbase, key, i);
+        p[i] = ok ? p[i] : 0.0f;
+        ds[i] = ok ? ds[i] : 0.0f;
+      }
+    }
     if constexpr (DBIAS != 0) {
       // dBias[q][key] = dS; rows past the sample end fall outside the
       // descriptor, and a lane whose key is past the end stores out of range
@@ -413,7 +443,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       const rsrc_t rdbr = make_rsrc(reinterpret_cast<const char*>(A_dbias) +
                                         (x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk) * ESB,
                                     (uint32_t)x.s.lq * x.s.lk * ESB);
-      const uint32_t vb = key < x.s.lk ? (uint32_t)(((t * QS + wq * 32 + g * 4) * x.s.lk + key) * ESB)
+      const uint32_t vb = key < x.s.lk ? (uint32_t)(((step_row0(x, t) + wq * 32 + g * 4) * x.s.lk + key) * ESB)
                                        : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -501,8 +531,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     uint32_t vb = 0;
     if constexpr (DBIAS != 0) {
       const int key = x.kt * KT + wv * 32 + l32;
-      vb = key < x.s.lk ? (uint32_t)(((t * QS + wq * 32 + g * 4) * x.s.lk + key) * ESB) : 0x80000000u;
+      vb = key < x.s.lk ? (uint32_t)(((step_row0(x, t) + wq * 32 + g * 4) * x.s.lk + key) * ESB) : 0x80000000u;
     }
+    const int wkey = x.kt * KT + wv * 32 + l32;
+    const int wrbase = WIN ? step_row0(x, t) + wq * 32 + g * 4 : 0;
     bf16x8 qa[NKK], oa[NKK];
     qa[0] = rows_frag<D, PAD>(qn, wq * 32 + l32, 0, g);
     oa[0] = rows_frag<D, PAD>(on, wq * 32 + l32, 0, g);
@@ -537,6 +569,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const float xv = BIAS ? fmaf(sv, A_scale, bias[c]) : sv * A_scale;
         p[c] = act_fwd(ACT, xv);
         ds[c] = act_grad(ACT, xv) * dpv;
+      }
+      if constexpr (WIN) {
+        const bool ok = window_ok(x, wkey - wrbase, wrbase, wkey, c);
+        p[c] = ok ? p[c] : 0.0f;
+        ds[c] = ok ? ds[c] : 0.0f;
       }
       if constexpr (DBIAS != 0) {
         const rsrc_t rdbr = make_rsrc(
@@ -582,7 +619,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(A_bias) + (A_bias_elems - 1), 2);
           const uint16_t last = buf_load2(rl, 0);
           char* bt = smem + st * Sh::STAGE + Sh::OFF_B;
-          *reinterpret_cast<uint16_t*>(bt + ((x.s.lq - 1) - t * QS) * Sh::BT::PITCH + ((x.s.lk - 1) - x.kt * KT) * 2) = last;
+          *reinterpret_cast<uint16_t*>(bt + ((x.s.lq - 1) - step_row0(x, t)) * Sh::BT::PITCH +
+                                       ((x.s.lk - 1) - x.kt * KT) * 2) = last;
         }
         __syncthreads();
       }

@@ -12,10 +12,18 @@ typedef float f32;
 
 namespace {
 
-template <int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT>
+template <int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT, bool WIN = false>
 hipError_t dkdv2_one(const BwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv2_kernel<J_TG, D, WKV, WKQ, ACT, BIAS, DBIAS, SPLIT>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkdv2_kernel<J_TG, D, WKV, WKQ, ACT, BIAS, DBIAS, SPLIT, WIN>), dim3(grid), dim3(256), 0, st,
+                     a);
   return hipGetLastError();
+}
+// sliding window: 128-key units, 32-query steps, no dBias
+template <int ACT>
+hipError_t dkdv2_window(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.wkv != 4 || k.dbias) return hipErrorInvalidValue;
+  if (k.bias) return k.split ? dkdv2_one<J_D, 4, 1, ACT, true, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, true, 0, false, true>(a, grid, st);
+  return k.split ? dkdv2_one<J_D, 4, 1, ACT, false, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, false, 0, false, true>(a, grid, st);
 }
 
 template <int D, int WKV, int WKQ, int ACT, bool SPLIT>
@@ -47,6 +55,11 @@ hipError_t dkdv2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream
 #define JATTN_DKDV2_NAME(D, TG) JATTN_DKDV2_NAME_(D, TG)
 
 hipError_t JATTN_DKDV2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.window) {
+    if (k.act == kSoftmax) return dkdv2_window<kSoftmax>(a, k, grid, st);
+    if (k.act == kGelu) return dkdv2_window<kGelu>(a, k, grid, st);
+    return dkdv2_window<kSilu>(a, k, grid, st);
+  }
   if (k.wkv == 4) return dkdv2_shape<J_D, 4, 1>(a, k, grid, st);
   if (k.wkv == 2) return dkdv2_shape<J_D, 2, 2>(a, k, grid, st);
   if constexpr (J_D == 128) {

@@ -154,6 +154,29 @@ __device__ __forceinline__ float wave_xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sliding window ("Training GEM at LLM scale", section "BlockAttention":
+// each token attends only to nearby tokens; the window kernel never visits
+// tiles outside the window).  Query row i sees key j iff
+// i - left <= j <= i + right, both inside the sample.
+struct Window {
+  int left, right, lq, lk;
+  // every pair of rows r0..r0+31 x keys k0..k0+31 is visible
+  __device__ __forceinline__ bool full(int r0, int k0) const {
+    return k0 + 31 - r0 <= right && r0 + 31 - k0 <= left && k0 + 31 < lk && r0 + 31 < lq;
+  }
+  __device__ __forceinline__ bool allows(int r, int k) const {
+    return k - r <= right && r - k <= left && k < lk && r < lq;
+  }
+};
+// First inner-loop step of a windowed unit whose own tile starts at row r0;
+// its partners start at max(0, r0 - near).
+__device__ __forceinline__ int window_first_step(int r0, int near, int step_rows) {
+  return max(0, r0 - near) / step_rows;
+}
+// A masked score in log2 units; a running max starts no lower than kNoScore
+// so that a row whose first keys are all masked stays finite.
+constexpr float kNoScore = -16384.0f;
+
 // erf-GELU and SiLU (GDPA activations) and their derivatives, fp32.
 __device__ __forceinline__ float act_fwd(int act, float x) {
   if (act == kGelu) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));

@@ -19,6 +19,10 @@
 // are stored permuted within each 32-key block (RowLoader PERM), so that the
 // 16 scores of a lane are 16 consecutive keys and its bias values are two
 // aligned 16-byte LDS reads.
+//
+// Sliding window (WIN, section "BlockAttention"): the unit's steps start at
+// the first key tile its window meets; dS is zeroed element-wise in 32x32
+// blocks that are not wholly inside the window.
 #pragma once
 #include "common.hpp"
 #include "fwd_impl.hpp"
@@ -54,7 +58,7 @@ struct Dq2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
+template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   using Sh = Dq2Shape<D, WQ, WK, BIAS>;
   constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW;
@@ -103,17 +107,22 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   // units that a compiler cannot keep in registers lands in scratch, whose
   // accesses wait on vmcnt and with it on the LDS prefetches.
   auto bias_elem0 = [&](const UnitInfo& x) { return x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk; };
+  // key tile of step t (a windowed unit starts at its window's first tile)
+  auto key_tile = [&](const UnitInfo& x, int t) {
+    return WIN ? window_first_step(x.qt * BM, a.win_l, BN) + t : t;
+  };
   auto issue_step = [&](const UnitInfo& x, int t, int st) {
     const uint32_t sb = smem_lds + st * Sh::STAGE;
-    const int64_t row0 = (int64_t)t * BN;
-    const int64_t rec = (int64_t)(x.s.lk - t * BN) * HD * 2;
+    const int kt = key_tile(x, t);
+    const int64_t row0 = (int64_t)kt * BN;
+    const int64_t rec = (int64_t)(x.s.lk - kt * BN) * HD * 2;
     kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
     vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
     if constexpr (BIAS) {
       // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
       if (t == 0) bload.init(wave, lane, x.s.lk);
       const int64_t e0 = bias_elem0(x);
-      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + (int64_t)t * BN) * 2;
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
       const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
       bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
     }
@@ -176,6 +185,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
       const char* kt = stage_k(stage);
       const char* vt = stage_v(stage);
       const int kb = wk * 32;  // this wave's key block inside the step
+      const int key0 = key_tile(cur, t) * BN + kb;  // its first key
 
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
       {
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
       // with a bias, slot i of this lane holds key t*BN + kb + 16g + i of
       // query row qt*BM + wq*32 + l32 (else key t*BN + kb + acc_row(i, g))
       float ds[16];
-      const int rem = cur.s.lk - (t * BN + kb + (BIAS ? 16 * g : 0));  // keys >= lk: slot key >= rem
+      const int rem = cur.s.lk - (key0 + (BIAS ? 16 * g : 0));  // keys >= lk: slot key >= rem
       if constexpr (BIAS) {
         const char* bt = stage_b(stage) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
         bf16x8_to_f32(bt, ds);
@@ -227,7 +237,16 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
           ds[i] = act_grad(ACT, x) * dpacc[i];
         }
       }
-      if (t + 1 == n) {
+      if constexpr (WIN) {
+        // pairs outside the window and keys past the sample end add nothing
+        const Window w{a.win_l, a.win_r, cur.s.lq, cur.s.lk};
+        const int row0 = cur.qt * BM + wq * 32;
+        if (!w.full(row0, key0)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            ds[i] = w.allows(row0 + l32, key0 + (BIAS ? 16 * g + i : acc_row(i, g))) ? ds[i] : 0.0f;
+        }
+      } else if (t + 1 == n) {
         // keys past the sample end (zero K/V rows, bias of the next row): their
         // dS must be exactly zero, whatever P overflowed to
 #pragma unroll

@@ -12,10 +12,18 @@ typedef float f32;
 
 namespace {
 
-template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
+template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 hipError_t dq2_one(const BwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((dq2_kernel<J_TG, J_D, WQ, WK, ACT, BIAS, SPLIT>), dim3(grid), dim3(64 * WQ * WK), 0, st, a);
+  hipLaunchKernelGGL((dq2_kernel<J_TG, J_D, WQ, WK, ACT, BIAS, SPLIT, WIN>), dim3(grid), dim3(64 * WQ * WK), 0,
+                     st, a);
   return hipGetLastError();
+}
+// sliding window: 128-row query tiles, 64-key steps only
+template <int ACT>
+hipError_t dq2_window(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.wq != 4) return hipErrorInvalidValue;
+  if (k.bias) return k.split ? dq2_one<4, 2, ACT, true, true, true>(a, grid, st) : dq2_one<4, 2, ACT, true, false, true>(a, grid, st);
+  return k.split ? dq2_one<4, 2, ACT, false, true, true>(a, grid, st) : dq2_one<4, 2, ACT, false, false, true>(a, grid, st);
 }
 
 template <int WQ, int WK, int ACT>
@@ -44,6 +52,11 @@ hipError_t dq2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t
 #define JATTN_DQ2_NAME(D, TG) JATTN_DQ2_NAME_(D, TG)
 
 hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.window) {
+    if (k.act == kSoftmax) return dq2_window<kSoftmax>(a, k, grid, st);
+    if (k.act == kGelu) return dq2_window<kGelu>(a, k, grid, st);
+    return dq2_window<kSilu>(a, k, grid, st);
+  }
   if (k.wq == 4) return dq2_shape<4, 2>(a, k, grid, st);
   return dq2_shape<1, 4>(a, k, grid, st);
 }

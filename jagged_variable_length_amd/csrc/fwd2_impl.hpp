@@ -21,6 +21,12 @@
 // scores a lane holds 16 consecutive keys: the lane's bias values are then
 // two aligned 16-byte LDS reads.  The key-split partials of one query group
 // are combined through LDS at the end of a unit.
+//
+// Sliding window (WIN, section "BlockAttention"): the unit's steps start at
+// the first key tile its window meets (the plan counts only the steps that
+// meet it); 32x32 blocks that are not wholly inside the window, or that hold
+// keys past the sample end, are masked element-wise, so no padding
+// correction is needed.
 #pragma once
 #include <type_traits>
 
@@ -64,7 +70,7 @@ struct Fwd2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
+template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   using Sh = Fwd2Shape<D, WQ, WK, BIAS>;
   constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW;
@@ -115,19 +121,24 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   // units that a compiler cannot keep in registers lands in scratch, whose
   // accesses wait on vmcnt and with it on the LDS prefetches.
   auto bias_elem0 = [&](const UnitInfo& x) { return x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk; };
+  // key tile of step t (a windowed unit starts at its window's first tile)
+  auto key_tile = [&](const UnitInfo& x, int t) {
+    return WIN ? window_first_step(x.qt * BM, a.win_l, BN) + t : t;
+  };
   // issue the HBM -> LDS loads of step t of unit x into stage st: the K and V
   // descriptors start at the step's first key row and end at the sample end
   auto issue_step = [&](const UnitInfo& x, int t, int st) {
     const uint32_t sb = smem_lds + st * Sh::STAGE;
-    const int64_t row0 = (int64_t)t * BN;
-    const int64_t rec = (int64_t)(x.s.lk - t * BN) * HD * 2;
+    const int kt = key_tile(x, t);
+    const int64_t row0 = (int64_t)kt * BN;
+    const int64_t rec = (int64_t)(x.s.lk - kt * BN) * HD * 2;
     kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
     vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
     if constexpr (BIAS) {
       // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
       if (t == 0) bload.init(wave, lane, x.s.lk);
       const int64_t e0 = bias_elem0(x);
-      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + (int64_t)t * BN) * 2;
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
       const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
       bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
     }
@@ -175,6 +186,17 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       const char* kt = stage_k(stage);
       const char* vt = stage_v(stage);
       const int kb = wk * 32;  // this wave's key block inside the step
+      const int key0 = key_tile(cur, t) * BN + kb;  // its first key
+      // window mask of this wave's 32x32 block (slot keys as described below)
+      auto mask = [&](float* v, float fill) {
+        const Window w{a.win_l, a.win_r, cur.s.lq, cur.s.lk};
+        const int row0 = cur.qt * BM + wq * 32;
+        if (!w.full(row0, key0)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            v[i] = w.allows(row0 + l32, key0 + (BIAS ? 16 * g + i : acc_row(i, g))) ? v[i] : fill;
+        }
+      };
 
       f32x16 sacc = f32x16{};
 #pragma unroll
@@ -192,7 +214,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         if (t + 1 == n) {
           // keys past the sample end carry the next row's bias: they must add
           // nothing (the subtraction below assumes a zero score)
-          const int rem = cur.s.lk - (t * BN + kb + 16 * g);
+          const int rem = cur.s.lk - (key0 + 16 * g);
 #pragma unroll
           for (int i = 0; i < 16; ++i) p[i] = i < rem ? p[i] : 0.0f;
           if (bias_elem0(cur) + (int64_t)cur.s.lq * cur.s.lk == a.bias_elems) {
@@ -214,14 +236,17 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i) {
           const float c = BIAS ? fmaf(p[i], kLog2e, -m_run) : -m_run;
           p[i] = fmaf(sacc[i], a.scale_log2, c);
-          mx = fmaxf(mx, p[i]);
         }
+        if constexpr (WIN) mask(p, -INFINITY);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, p[i]);
         mx = wave_xor32_max(mx);
         if constexpr (FIRST) {
-          // the running max starts at this step's max (m_run was 0)
-          m_run = mx;
+          // the running max starts at this step's max (m_run was 0); with a
+          // window the step may hold no visible key of the row
+          m_run = WIN ? fmaxf(mx, kNoScore) : mx;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) p[i] -= mx;
+          for (int i = 0; i < 16; ++i) p[i] -= m_run;
         } else {
           if (__builtin_amdgcn_ballot_w64(mx > kLazy) != 0) {
             const float delta = fmaxf(mx, 0.0f);
@@ -259,6 +284,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           const float x = BIAS ? p[i] + sacc[i] * a.scale : sacc[i] * a.scale;
           p[i] = act_fwd(ACT, x);
         }
+        if constexpr (WIN) mask(p, 0.0f);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           pf[st] = pack8(&p[st * 8]);
@@ -291,12 +317,18 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
 
     // ---- epilogue ----
     if constexpr (SOFTMAX) {
-      // keys past the sample end entered the last step as zeros
-      int npad = 0;
-      if (n > 0) npad = 32 - min(max(cur.s.lk - ((n - 1) * BN + wk * 32), 0), 32);
-      const float pad_e = fast_exp2(-m_run);
-      l_run = wave_xor32_sum(l_run) - (float)npad * pad_e;
-      lr_run = wave_xor32_sum(lr_run) - (float)npad * (float)(bf16)pad_e;
+      l_run = wave_xor32_sum(l_run);
+      lr_run = wave_xor32_sum(lr_run);
+      if constexpr (!WIN) {
+        // keys past the sample end entered the last step as zeros.  (A window
+        // masks them instead; its running max may sit at kNoScore, where
+        // 2^-m overflows.)
+        int npad = 0;
+        if (n > 0) npad = 32 - min(max(cur.s.lk - ((n - 1) * BN + wk * 32), 0), 32);
+        const float pad_e = fast_exp2(-m_run);
+        l_run -= (float)npad * pad_e;
+        lr_run -= (float)npad * (float)(bf16)pad_e;
+      }
       if (cur.s.lk <= wk * 32) {
         // this wave's key block lies wholly past the sample end: it holds no
         // term of the row (its O is zero since those V rows read as zero)

@@ -9,10 +9,27 @@
 namespace jattn {
 
 namespace {
-template <typename TO, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
+template <typename TO, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 hipError_t one(const FwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd2_kernel<TO, J_D, WQ, WK, ACT, BIAS, SPLIT>), dim3(grid), dim3(64 * WQ * WK), 0, st, a);
+  hipLaunchKernelGGL((fwd2_kernel<TO, J_D, WQ, WK, ACT, BIAS, SPLIT, WIN>), dim3(grid), dim3(64 * WQ * WK), 0, st,
+                     a);
   return hipGetLastError();
+}
+// sliding window: 128-row query tiles, 64-key steps only
+template <typename TO, int ACT>
+hipError_t window_act(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.bias) return k.split ? one<TO, 4, 2, ACT, true, true, true>(a, grid, st) : one<TO, 4, 2, ACT, true, false, true>(a, grid, st);
+  return k.split ? one<TO, 4, 2, ACT, false, true, true>(a, grid, st) : one<TO, 4, 2, ACT, false, false, true>(a, grid, st);
+}
+template <typename TO>
+hipError_t window(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.wq != 4) return hipErrorInvalidValue;
+  if (k.act == kSoftmax) {
+    if (k.bias) return one<TO, 4, 2, kSoftmax, true, false, true>(a, grid, st);
+    return one<TO, 4, 2, kSoftmax, false, false, true>(a, grid, st);
+  }
+  if (k.act == kGelu) return window_act<TO, kGelu>(a, k, grid, st);
+  return window_act<TO, kSilu>(a, k, grid, st);
 }
 template <typename TO, int WQ, int WK>
 hipError_t shape_all(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
@@ -41,6 +58,7 @@ hipError_t shape_all(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t
 }
 template <typename TO>
 hipError_t dispatch(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if (k.window) return window<TO>(a, k, grid, st);
   // 4 query groups x 2 key halves (64-key steps), or 1 query group x 4 key
   // quarters (128-key steps) for short queries
   if (k.wq == 4) return shape<TO, 4, 2>(a, k, grid, st);

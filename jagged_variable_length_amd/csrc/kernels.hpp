@@ -27,6 +27,7 @@ struct FwdArgs {
   float scale;       // softmax / activation scale
   float scale_log2;  // scale * log2(e)
   int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
+  int win_l, win_r;    // sliding window: query i sees keys i - win_l .. i + win_r
 };
 
 struct DiArgs {
@@ -58,6 +59,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
+  int win_l, win_r;    // sliding window: query i sees keys i - win_l .. i + win_r
 };
 
 // Which template instance to run.
@@ -72,6 +74,7 @@ struct KernelSel {
   bool out_f32;   // O (fwd) or dQ/dK/dV (bwd) are fp32 (else bf16)
   int wq;         // fwd/dq: waves along queries (4 or 1; 1 => 4-way key split)
   int wkv;        // dkdv: waves along keys (4, 2 or 1; the rest split queries)
+  bool window;    // sliding-window mask (bf16 inputs; wq = 4, wkv = 4)
 };
 
 #define JATTN_FWD_LAUNCHER_(D, TI, TO) launch_fwd_##D##_##TI##_##TO

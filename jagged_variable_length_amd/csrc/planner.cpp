@@ -15,10 +15,22 @@ struct Unit {
   int32_t b, h, t, cost;
 };
 
+// Steps of a windowed unit: tile t (tile_rows rows of n_tile) meets partner
+// rows row - near .. row + far of n_step; returns the step count.
+int32_t window_cost(int32_t t, int32_t tile_rows, int32_t step_rows, int32_t n_tile, int32_t n_step,
+                    int64_t near, int64_t far) {
+  const int64_t r0 = (int64_t)t * tile_rows;
+  const int64_t r1 = std::min<int64_t>(n_tile, r0 + tile_rows) - 1;
+  const int64_t first = std::max<int64_t>(0, r0 - near);
+  const int64_t last = std::min<int64_t>(n_step - 1, r1 + far);
+  if (last < first) return 0;
+  return (int32_t)(last / step_rows - first / step_rows + 1);
+}
+
 }  // namespace
 
 void plan_units(UnitKind kind, const std::vector<int32_t>& lq, const std::vector<int32_t>& lk, int H,
-                int tile_rows, int step_rows, int num_workers, Order order, UnitList* out) {
+                int tile_rows, int step_rows, int num_workers, Order order, UnitList* out, Window win) {
   out->tile_rows = tile_rows;
   out->step_rows = step_rows;
   out->num_workers = num_workers;
@@ -48,8 +60,15 @@ void plan_units(UnitKind kind, const std::vector<int32_t>& lq, const std::vector
         cost = 1;
         break;
     }
+    const bool windowed = win.on() && kind != kKindBlock;
     for (int h = 0; h < H; ++h)
-      for (int t = 0; t < n_tiles; ++t) all.push_back(Unit{b, h, t, cost});
+      for (int t = 0; t < n_tiles; ++t) {
+        int32_t c = cost;
+        if (windowed)
+          c = kind == kKindDkdv ? window_cost(t, tile_rows, step_rows, lk[b], lq[b], win.right, win.left)
+                                : window_cost(t, tile_rows, step_rows, lq[b], lk[b], win.left, win.right);
+        all.push_back(Unit{b, h, t, c});
+      }
   }
 
   // 2. stable sort by cost, descending

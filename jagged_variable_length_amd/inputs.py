@@ -46,6 +46,7 @@ class Workload:
     grad_dtype: str
     split_operands: bool
     dbias_dtype: str = "f32"
+    window: Optional[tuple] = None  # sliding window (left, right), self-attention only
 
 
 WORKLOADS = {
@@ -54,6 +55,9 @@ WORKLOADS = {
     2: Workload("cross_longq_shortkv", 512, 8, 64, "bf16", ACT_SOFTMAX, False, False, False, "bf16", "f32", True),
     3: Workload("gdpa_pma_gelu", 256, 8, 128, "bf16", ACT_GELU, False, False, False, "f32", "f32", True),
     4: Workload("block_attention_64", 64, 4, 128, "bf16", ACT_SOFTMAX, True, False, False, "bf16", "bf16", False),
+    # sliding-window self-attention over long sequences (lengths as workload 4)
+    5: Workload("swa_long_w256", 64, 4, 128, "bf16", ACT_SOFTMAX, False, False, False, "bf16", "bf16", False,
+                window=(256, 256)),
 }
 
 
@@ -110,7 +114,7 @@ def _lengths_from(rng, cfg):
         lq = np.full(w.B, 32, dtype=np.int64)
         lk = _lognormal_lengths(rng, w.B, 1500, 64, 4000)
         return lq, lk
-    if cfg == 4:
+    if cfg in (4, 5):
         lq = rng.integers(2048, 16385, w.B).astype(np.int64)
         return lq, lq.copy()
     raise ValueError(f"unknown workload {cfg}")

@@ -20,11 +20,12 @@ def say(*a):
 
 
 def make_op(inp: gen.JaggedInputs, *, act="softmax", block=False, bias=False, want_dbias=False,
-            out_dtype=None, grad_dtype=None, split=False, order="zigzag", num_workers=0, dbias_dtype=None):
+            out_dtype=None, grad_dtype=None, split=False, order="zigzag", num_workers=0, dbias_dtype=None,
+            window=None):
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, inp.H, inp.D, act=act, block_diagonal=block,
                            has_bias=bias, want_dbias=want_dbias, in_dtype=inp.dtype, out_dtype=out_dtype,
                            grad_dtype=grad_dtype, split_operands=split, order=order,
-                           num_workers=num_workers, dbias_dtype=dbias_dtype)
+                           num_workers=num_workers, dbias_dtype=dbias_dtype, window=window)
     return op.upload()
 
 
@@ -38,14 +39,14 @@ def device_inputs(inp: gen.JaggedInputs):
 def oracle_fwd(inp, op):
     return ora.forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_offsets, inp.kv_offsets,
                        scale=op.scale, activation=op.act, block_diagonal=op.block_diagonal,
-                       bias=inp.f64("bias"))
+                       bias=inp.f64("bias"), window=op.window)
 
 
 def oracle_bwd(inp, op):
     return ora.backward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("dout"), inp.q_offsets,
                         inp.kv_offsets, scale=op.scale, activation=op.act,
                         block_diagonal=op.block_diagonal, bias=inp.f64("bias"),
-                        want_dbias=op.want_dbias)
+                        want_dbias=op.want_dbias, window=op.window)
 
 
 def max_err(got: np.ndarray, ref: np.ndarray, name: str):

@@ -55,6 +55,7 @@ def _desc(**kw):
     d.split_operands = kw.get("split", 0)
     d.order = kw.get("order", B.JATTN_HEAVY_FIRST)
     d.num_workers = kw.get("num_workers", 0)
+    d.window_left, d.window_right = kw.get("window", (0, 0))
     return d
 
 
@@ -77,6 +78,13 @@ def _desc(**kw):
     (dict(mask=B.JATTN_MASK_BLOCKDIAG64, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
      [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
     (dict(mask=B.JATTN_MASK_BLOCKDIAG64, num_workers=7), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(mask=3), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(mask=B.JATTN_MASK_WINDOW), [0, 3, 5], [0, 2, 4], B.JATTN_E_SHAPE),  # lq != lk
+    (dict(mask=B.JATTN_MASK_WINDOW, window=(-1, 4)), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(mask=B.JATTN_MASK_WINDOW, window=(4, -2)), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(mask=B.JATTN_MASK_WINDOW, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
+     [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(mask=B.JATTN_MASK_WINDOW, has_bias=1, want_dbias=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
 ])
 def test_plan_create_rejects(lib, kw, qo, ko, code):
     d = _desc(**kw)
@@ -211,3 +219,36 @@ def test_empty_batch_plans(lib):
         B.jattn_fwd(p, None, None, None, None, None, None, None, None)
     finally:
         B.jattn_plan_destroy(p)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_window_plans_match(lib, seed):
+    """Windowed plans (tile skipping) bit-exact against the reference planner,
+    and the plan's pair count against brute force."""
+    rng = np.random.default_rng(200 + seed)
+    Bn = int(rng.integers(1, 30))
+    L = rng.integers(0, 700, Bn)
+    L[0] = 0
+    qo = gen.offsets_from_lengths(L)
+    W = int(rng.integers(1, 40))
+    window = [(0, 0), (5, 130), (200, 0), (63, 64), (2 ** 31 - 1, 1), (1000, 1000)][seed]
+    D = [32, 64, 128][seed % 3]
+    for order in range(3):
+        d = _desc(B=Bn, H=3, D=D, order=order, num_workers=W, mask=B.JATTN_MASK_WINDOW, window=window,
+                  act=seed % 3)
+        p = B.jattn_plan_create(d, qo, qo)
+        try:
+            info, parts = _compare_plan(p, L, L, 3, False)
+            assert (info.fwd.tile_rows, info.dq.tile_rows, info.dkdv.tile_rows) == (128, 128, 128)
+            for kind, which, kp in parts:
+                units = B.jattn_plan_export(p, which * 2).reshape(-1, 4)
+                offs = B.jattn_plan_export(p, which * 2 + 1)
+                ref_u, ref_o = P.plan(kind, L.tolist(), L.tolist(), 3, kp.tile_rows, kp.step_rows, W,
+                                      ["heavy_first", "zigzag", "lpt"][order], window=window)
+                np.testing.assert_array_equal(units, np.array(ref_u, np.int32).reshape(-1, 4))
+                np.testing.assert_array_equal(offs, np.array(ref_o, np.int32))
+            left, right = window
+            pairs = sum(sum(min(n - 1, i + right) - max(0, i - left) + 1 for i in range(n)) for n in L.tolist())
+            assert info.flops_fwd == pytest.approx(4.0 * 3 * D * pairs, rel=1e-12)
+        finally:
+            B.jattn_plan_destroy(p)
