@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (1 = headline)")
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..5 (1 = headline)")
     ap.add_argument("--order", default="zigzag", help="unit order across workers (the zigzag deal by default)")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,8 +184,14 @@ def traffic_summary(args):
     print(json.dumps(out, indent=1))
 
 
+def _window_pairs(n, window):
+    left, right = window
+    return sum(min(n - 1, i + right) - max(0, i - left) + 1 for i in range(n))
+
+
 def cpu_baseline(w, inp, budget_s):
-    """fp64 oracle, fwd+bwd, samples in order until the time budget is spent."""
+    """fp64 oracle, fwd+bwd, samples in order until the time budget is spent
+    (shortest first for the sliding-window workload, whose samples are long)."""
     from oracle import attention as ora
     try:
         from threadpoolctl import threadpool_info
@@ -196,18 +202,24 @@ def cpu_baseline(w, inp, budget_s):
     do, bias = inp.f64("dout"), inp.f64("bias")
     scale = 1.0 / np.sqrt(w.D)
     # warm-up on a small sample
-    ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, 0, scale=scale, activation=w.act,
-                       block_diagonal=w.block_diagonal, bias=bias)
     lq, lk = inp.lq, inp.lk
-    flops, n = 0.0, 0
+    order = list(np.argsort(lq, kind="stable")) if w.window is not None else list(range(inp.B))
+    ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, int(order[0]), scale=scale, activation=w.act,
+                       block_diagonal=w.block_diagonal, bias=bias, window=w.window)
+    flops, n, done = 0.0, 0, []
     t0 = time.perf_counter()
-    for b in range(inp.B):
+    for b in order:
+        b = int(b)
         ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
-                           block_diagonal=w.block_diagonal, bias=bias)
+                           block_diagonal=w.block_diagonal, bias=bias, window=w.window)
         ora.backward_sample(q, k, v, do, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
-                            block_diagonal=w.block_diagonal, bias=bias, want_dbias=w.want_dbias)
+                            block_diagonal=w.block_diagonal, bias=bias, want_dbias=w.want_dbias,
+                            window=w.window)
+        done.append(b)
         if w.block_diagonal:
             pairs = sum(min(64, int(lq[b]) - s) ** 2 for s in range(0, int(lq[b]), 64))
+        elif w.window is not None:
+            pairs = _window_pairs(int(lq[b]), w.window)
         else:
             pairs = int(lq[b]) * int(lk[b])
         flops += 3.5 * 4.0 * w.H * w.D * pairs
@@ -215,8 +227,10 @@ def cpu_baseline(w, inp, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    which = f"samples 0..{n - 1}" if w.window is None else \
+        f"the {n} shortest samples (lengths {int(lq[done[0]])}..{int(lq[done[-1]])})"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s"}
+            "sample": f"{which} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s"}
 
 
 def main():
@@ -244,7 +258,7 @@ def main():
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
                            has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
-                           num_workers=args.workers, dbias_dtype=w.dbias_dtype)
+                           num_workers=args.workers, dbias_dtype=w.dbias_dtype, window=w.window)
     t0 = time.perf_counter()
     plan_ms = None
     op.upload()
@@ -344,7 +358,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; lengths and value distributions of the workload)",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} D={w.D} {w.dtype} act={w.act}"
-                               f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}",
+                               f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}"
+                               f"{f' window={w.window}' if w.window else ''}",
                    "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk, "seed": cfg,
                    "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),
                    "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype,
