@@ -67,6 +67,36 @@ def silu_grad(x):
     return s * (1.0 + x * (1.0 - s))
 
 
+# ALU-only GELU ("Generalized Dot-Product Attention (GDPA)", item on the
+# ALU-only activation approximation): GELU in its tanh form,
+#   0.5 x (1 + tanh(c (x + a x^3))),  c = sqrt(2/pi), a = 0.044715
+# (Hendrycks and Gimpel's approximation), with tanh replaced by its Taylor
+# polynomial about 0 through order 6.  tanh is odd, so its even coefficients
+# vanish: t(u) = u - u^3/3 + 2 u^5/15.  Accurate only for bounded inputs,
+# which QK-norm provides (see qk_norm below).
+GELU_TANH_C = math.sqrt(2.0 / math.pi)
+GELU_TANH_A = 0.044715
+
+
+def tanh_taylor6(u):
+    return u - u ** 3 / 3.0 + 2.0 * u ** 5 / 15.0
+
+
+def tanh_taylor6_grad(u):
+    return 1.0 - u ** 2 + 2.0 * u ** 4 / 3.0
+
+
+def gelu_poly(x):
+    u = GELU_TANH_C * (x + GELU_TANH_A * x ** 3)
+    return 0.5 * x * (1.0 + tanh_taylor6(u))
+
+
+def gelu_poly_grad(x):
+    u = GELU_TANH_C * (x + GELU_TANH_A * x ** 3)
+    du = GELU_TANH_C * (1.0 + 3.0 * GELU_TANH_A * x ** 2)
+    return 0.5 * (1.0 + tanh_taylor6(u)) + 0.5 * x * tanh_taylor6_grad(u) * du
+
+
 def identity(x):
     return x
 
@@ -78,6 +108,7 @@ def identity_grad(x):
 _ACTS = {
     "gelu": (gelu, gelu_grad),
     "silu": (silu, silu_grad),
+    "gelu_poly": (gelu_poly, gelu_poly_grad),
     "identity": (identity, identity_grad),
 }
 
