@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..5 (1 = headline)")
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..6 (1 = headline)")
     ap.add_argument("--order", default="zigzag", help="unit order across workers (the zigzag deal by default)")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -86,6 +86,11 @@ def kernel_work(w, info, es_in, es_out, es_g, es_db=4):
     }
     if soft:
         work["prep"] = (qd * es_out + qd * es_in + rowstat, 2.0 * qd)
+    if w.qk_norm:
+        # read Q and K, write their normalised copies and 1/||row||; the
+        # backward reads Q, K and the gradients of the copies, writes dQ, dK
+        work["qknorm"] = (2 * (qd + kd) * es_in + (Tq + Tk) * H * 4, 3.0 * (qd + kd))
+        work["qknorm_bwd"] = ((qd + kd) * es_in + 2 * (qd + kd) * es_g, 6.0 * (qd + kd))
     return work
 
 
@@ -100,7 +105,7 @@ def source_hash():
 
 KERNEL_KEYS = [("block_fwd_kernel", "block_fwd"), ("block_bwd_kernel", "block_bwd"), ("dkdv", "dkdv"),
                ("dq2_kernel", "dq"), ("dq_kernel", "dq"), ("fwd2_kernel", "fwd"), ("fwd_kernel", "fwd"),
-               ("di_kernel", "prep")]
+               ("di_kernel", "prep"), ("l2norm_fwd_kernel", "qknorm"), ("l2norm_bwd_kernel", "qknorm_bwd")]
 
 
 def kernel_key(name):
@@ -200,7 +205,9 @@ def cpu_baseline(w, inp, budget_s):
         cores = None
     q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
     do, bias = inp.f64("dout"), inp.f64("bias")
-    scale = 1.0 / np.sqrt(w.D)
+    scale = 1.0 / np.sqrt(w.D) if w.scale is None else w.scale
+    if w.qk_norm:
+        return _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores)
     # warm-up on a small sample
     lq, lk = inp.lq, inp.lk
     order = list(np.argsort(lq, kind="stable")) if w.window is not None else list(range(inp.B))
@@ -233,6 +240,31 @@ def cpu_baseline(w, inp, budget_s):
             "sample": f"{which} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s"}
 
 
+def _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores):
+    """QK-norm, attention and both backwards per sample, in float64."""
+    from oracle import attention as ora
+    from oracle import qknorm as qn
+    flops, n = 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(inp.B):
+        sq = slice(int(inp.q_offsets[b]), int(inp.q_offsets[b + 1]))
+        sk = slice(int(inp.kv_offsets[b]), int(inp.kv_offsets[b + 1]))
+        off_q, off_k = np.array([0, sq.stop - sq.start]), np.array([0, sk.stop - sk.start])
+        qh, kh = qn.forward(q[sq])[0], qn.forward(k[sk])[0]
+        ora.forward(qh, kh, v[sk], off_q, off_k, scale=scale, activation=w.act)
+        dqh, dkh, _, _ = ora.backward(qh, kh, v[sk], do[sq], off_q, off_k, scale=scale, activation=w.act)
+        qn.backward(q[sq], dqh)
+        qn.backward(k[sk], dkh)
+        flops += 3.5 * 4.0 * w.H * w.D * int(inp.lq[b]) * int(inp.lk[b])
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), QK-norm + attention, fwd+bwd in "
+                      f"float64, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,7 +290,8 @@ def main():
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
                            has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
-                           num_workers=args.workers, dbias_dtype=w.dbias_dtype, window=w.window)
+                           num_workers=args.workers, dbias_dtype=w.dbias_dtype, window=w.window,
+                           scale=w.scale)
     t0 = time.perf_counter()
     plan_ms = None
     op.upload()
@@ -271,6 +304,14 @@ def main():
     dk = torch.empty(op.Tk, w.H, w.D, dtype=tdt[w.grad_dtype], device="cuda")
     dv = torch.empty_like(dk)
     dbias = torch.empty(int(op.info.bias_elems), dtype=tdt[w.dbias_dtype], device="cuda") if w.want_dbias else None
+    # attention inputs and the gradients it produces for them: the normalised
+    # copies of Q and K with QK-norm, else Q and K themselves
+    q_in, k_in, dq_att, dk_att = dev["q"], dev["k"], dq, dk
+    if w.qk_norm:
+        q_in, k_in = torch.empty_like(dev["q"]), torch.empty_like(dev["k"])
+        dq_att, dk_att = torch.empty_like(dq), torch.empty_like(dk)
+        rq = torch.empty(op.Tq, w.H, dtype=torch.float32, device="cuda")
+        rk = torch.empty(op.Tk, w.H, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     # plan creation cost (host only), measured on a fresh plan
     t1 = time.perf_counter()
@@ -283,15 +324,26 @@ def main():
                     ("block_bwd", lambda: op.backward(dev["q"], dev["k"], dev["v"], dev["dout"], dq=dq, dk=dk, dv=dv))]
     else:
         def fwd():
-            op.forward(dev["q"], dev["k"], dev["v"], bias=bias, o=o, lse=lse)
+            op.forward(q_in, k_in, dev["v"], bias=bias, o=o, lse=lse)
 
         def stage(s):
-            return lambda: op.backward(dev["q"], dev["k"], dev["v"], dev["dout"], o=o, lse=lse, bias=bias,
-                                       dq=dq, dk=dk, dv=dv, dbias=dbias, stages=s)
-        launches = [("fwd", fwd)]
+            return lambda: op.backward(q_in, k_in, dev["v"], dev["dout"], o=o, lse=lse, bias=bias,
+                                       dq=dq_att, dk=dk_att, dv=dv, dbias=dbias, stages=s)
+
+        def qknorm():
+            A.qk_norm(dev["q"], out=q_in, rnorm=rq)
+            A.qk_norm(dev["k"], out=k_in, rnorm=rk)
+
+        def qknorm_bwd():
+            A.qk_norm_backward(dev["q"], dq_att, out=dq)
+            A.qk_norm_backward(dev["k"], dk_att, out=dk)
+        launches = [("qknorm", qknorm)] if w.qk_norm else []
+        launches.append(("fwd", fwd))
         if w.act == "softmax":
             launches.append(("prep", stage(Bd.JATTN_BWD_PREP)))
         launches += [("dkdv", stage(Bd.JATTN_BWD_DKDV)), ("dq", stage(Bd.JATTN_BWD_DQ))]
+        if w.qk_norm:
+            launches.append(("qknorm_bwd", qknorm_bwd))
 
     for _ in range(args.warmup):
         for _, f in launches:
@@ -359,7 +411,8 @@ def main():
         "data": "synthetic (seeded; lengths and value distributions of the workload)",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} D={w.D} {w.dtype} act={w.act}"
                                f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}"
-                               f"{f' window={w.window}' if w.window else ''}",
+                               f"{f' window={w.window}' if w.window else ''}"
+                               f"{f' qk-norm scale={w.scale}' if w.qk_norm else ''}",
                    "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk, "seed": cfg,
                    "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),
                    "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype,

@@ -16,7 +16,9 @@
  * For sample b and head h, with Q_b [lq,D], K_b, V_b [lk,D]:
  *   S = scale * Q_b K_b^T + bias_b[h]
  *   softmax:  P = softmax_row(S), O = P V, LSE_i = ln sum_j exp(S_ij)
- *   GDPA:     P = act(S),        O = P V   (act = erf-GELU or SiLU)
+ *   GDPA:     P = act(S),        O = P V   (act = erf-GELU, SiLU, or the
+ *             ALU-only polynomial GELU of the GDPA section, which is accurate
+ *             on the bounded scores that QK-norm gives)
  *   block-diagonal: only pairs with floor(i/64) == floor(j/64) take part.
  *   sliding window (left, right): only pairs with i - left <= j <= i + right
  *     take part (self-attention: lq_b == lk_b).  The pages fix no window
@@ -72,6 +74,11 @@ extern "C" {
 #define JATTN_SOFTMAX 0
 #define JATTN_GELU_ERF 1 /* GDPA with x * Phi(x) */
 #define JATTN_SILU 2     /* GDPA with x * sigmoid(x) */
+#define JATTN_GELU_POLY 3 /* GDPA with the ALU-only GELU: 0.5 x (1 + t(u)),
+                             u = sqrt(2/pi) (x + 0.044715 x^3),
+                             t(u) = u - u^3/3 + 2 u^5/15 (tanh's Taylor
+                             polynomial through order 6); for the bounded
+                             scores of QK-norm inputs; bf16 inputs only */
 
 /* mask (desc.mask) */
 #define JATTN_MASK_NONE 0
@@ -197,6 +204,25 @@ int jattn_bwd_stages(const jattn_plan* plan, int32_t stages, const void* q, cons
                      void* stream);
 
 void jattn_plan_destroy(jattn_plan* plan);
+
+/* QK-norm ("Training GEM at LLM scale", section "Generalized Dot-Product
+ * Attention (GDPA)", item on the ALU-only activation: the polynomial GELU is
+ * accurate on the bounded input range that query/key normalisation
+ * enforces), read as row-wise L2 normalisation: each of `rows` rows of D
+ * contiguous elements (a [T, H, D] tensor has rows = T * H) becomes
+ *   y = x * r,   r = 1 / max(||x||_2, 1e-12),
+ * so that |q . k| <= 1 for normalised rows.  Forward writes y (y_dtype) and,
+ * if rnorm is not NULL, r per row (float32).  Backward, given dy = dL/dy,
+ * writes dx = r (dy - y (y . dy)) (the projection term only where
+ * ||x|| > 1e-12), recomputing y and r from x.  x, y, dy, dx: device memory,
+ * 16-byte aligned; D in {32, 64, 128}; dtypes JATTN_BF16 | JATTN_F32.  y may
+ * be x and dx may be dy when the element types match.  Enqueued on `stream`;
+ * errors as for the other calls (validated on the host, nothing launched on
+ * error; rows = 0 is a no-op). */
+int jattn_l2norm_fwd(const void* x, void* y, float* rnorm, int64_t rows, int32_t D, int32_t x_dtype,
+                     int32_t y_dtype, void* stream);
+int jattn_l2norm_bwd(const void* x, const void* dy, void* dx, int64_t rows, int32_t D, int32_t x_dtype,
+                     int32_t dy_dtype, int32_t dx_dtype, void* stream);
 
 /* Static text for a status code. */
 const char* jattn_strerror(int status);

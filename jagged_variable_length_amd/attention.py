@@ -12,7 +12,8 @@ import torch
 
 from . import binding as _b
 
-_ACT = {"softmax": _b.JATTN_SOFTMAX, "gelu": _b.JATTN_GELU_ERF, "silu": _b.JATTN_SILU}
+_ACT = {"softmax": _b.JATTN_SOFTMAX, "gelu": _b.JATTN_GELU_ERF, "silu": _b.JATTN_SILU,
+        "gelu_poly": _b.JATTN_GELU_POLY}
 _DT = {"bf16": _b.JATTN_BF16, "f32": _b.JATTN_F32}
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 _ORDER = {"heavy_first": _b.JATTN_HEAVY_FIRST, "zigzag": _b.JATTN_ZIGZAG, "lpt": _b.JATTN_LPT}
@@ -113,6 +114,35 @@ class JaggedAttention:
             _b.jattn_plan_destroy(self.plan)
         except Exception:
             pass
+
+
+_DT_OF = {torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+def qk_norm(x: torch.Tensor, out_dtype: Optional[str] = None, out: Optional[torch.Tensor] = None,
+            rnorm: Optional[torch.Tensor] = None):
+    """QK-norm forward: each row x[..., :] (last dim D) scaled to unit L2 length
+    by the library's kernel.  Returns (y, rnorm) with rnorm = 1 / max(||x||, eps)."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    odt = out_dtype or _DT_OF[x.dtype]
+    y = out if out is not None else torch.empty(x.shape, dtype=_TORCH_DT[odt], device=x.device)
+    r = rnorm if rnorm is not None else torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _b.jattn_l2norm_fwd(_ptr(x), _ptr(y), _ptr(r), rows, D, _DT[_DT_OF[x.dtype]], _DT[odt],
+                        torch.cuda.current_stream(x.device).cuda_stream)
+    return y, r
+
+
+def qk_norm_backward(x: torch.Tensor, dy: torch.Tensor, out_dtype: Optional[str] = None,
+                     out: Optional[torch.Tensor] = None):
+    """QK-norm backward: dL/dx from the forward input x and dL/dy."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    odt = out_dtype or _DT_OF[dy.dtype]
+    dx = out if out is not None else torch.empty(x.shape, dtype=_TORCH_DT[odt], device=x.device)
+    _b.jattn_l2norm_bwd(_ptr(x), _ptr(dy), _ptr(dx), rows, D, _DT[_DT_OF[x.dtype]], _DT[_DT_OF[dy.dtype]],
+                        _DT[odt], torch.cuda.current_stream(x.device).cuda_stream)
+    return dx
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:

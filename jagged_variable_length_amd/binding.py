@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjattn.so
 JATTN_OK = 0
 JATTN_E_NULL, JATTN_E_OFFSETS, JATTN_E_SHAPE, JATTN_E_UNSUPPORTED = -1, -2, -3, -4
 JATTN_E_ALIGN, JATTN_E_WORKSPACE, JATTN_E_STATE, JATTN_E_HIP, JATTN_E_ARG = -5, -6, -7, -8, -9
-JATTN_SOFTMAX, JATTN_GELU_ERF, JATTN_SILU = 0, 1, 2
+JATTN_SOFTMAX, JATTN_GELU_ERF, JATTN_SILU, JATTN_GELU_POLY = 0, 1, 2, 3
 JATTN_MASK_NONE, JATTN_MASK_BLOCKDIAG64, JATTN_MASK_WINDOW = 0, 1, 2
 JATTN_BF16, JATTN_F32 = 0, 1
 JATTN_HEAVY_FIRST, JATTN_ZIGZAG, JATTN_LPT = 0, 1, 2
@@ -27,7 +27,7 @@ JATTN_BWD_PREP, JATTN_BWD_DKDV, JATTN_BWD_DQ, JATTN_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
             "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_plan_destroy", "jattn_strerror",
-            "jattn_last_error"]
+            "jattn_last_error", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]
 
 
 class JattnError(RuntimeError):
@@ -86,8 +86,10 @@ def lib():
     L.jattn_strerror.restype = ctypes.c_char_p
     L.jattn_last_error.argtypes = []
     L.jattn_last_error.restype = ctypes.c_char_p
+    L.jattn_l2norm_fwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
+    L.jattn_l2norm_bwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, vp]
     for name in ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
-                 "jattn_fwd", "jattn_bwd", "jattn_bwd_stages"]:
+                 "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -141,6 +143,14 @@ def jattn_bwd(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, s
 
 def jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
     _check(lib().jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
+
+
+def jattn_l2norm_fwd(x, y, rnorm, rows, D, x_dtype, y_dtype, stream) -> None:
+    _check(lib().jattn_l2norm_fwd(x, y, rnorm, rows, D, x_dtype, y_dtype, stream))
+
+
+def jattn_l2norm_bwd(x, dy, dx, rows, D, x_dtype, dy_dtype, dx_dtype, stream) -> None:
+    _check(lib().jattn_l2norm_bwd(x, dy, dx, rows, D, x_dtype, dy_dtype, dx_dtype, stream))
 
 
 def jattn_plan_destroy(plan: int) -> None:

@@ -34,7 +34,8 @@ FWD_INST = [(128, "bf16", "bf16"), (128, "bf16", "f32"), (64, "bf16", "bf16"), (
 
 
 def units():
-    u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", [])]
+    u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", []),
+         ("l2norm.hip", "l2norm", [])]
     for d in (128, 64, 32):
         u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
         for tg in ("bf16", "f32"):

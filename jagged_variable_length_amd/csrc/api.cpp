@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <vector>
@@ -113,7 +114,9 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   if (d.B < 0) return fail(JATTN_E_SHAPE, "B must be >= 0");
   if (d.H < 1 || d.H > 4096) return fail(JATTN_E_SHAPE, "H must be in [1, 4096]");
   if (d.D != 32 && d.D != 64 && d.D != 128) return fail(JATTN_E_SHAPE, "D must be 32, 64 or 128");
-  if (d.act < JATTN_SOFTMAX || d.act > JATTN_SILU) return fail(JATTN_E_UNSUPPORTED, "unknown activation");
+  if (d.act < JATTN_SOFTMAX || d.act > JATTN_GELU_POLY) return fail(JATTN_E_UNSUPPORTED, "unknown activation");
+  if (d.act == JATTN_GELU_POLY && d.in_dtype != JATTN_BF16)
+    return fail(JATTN_E_UNSUPPORTED, "the polynomial GELU needs bf16 inputs");
   if (d.mask != JATTN_MASK_NONE && d.mask != JATTN_MASK_BLOCKDIAG64 && d.mask != JATTN_MASK_WINDOW)
     return fail(JATTN_E_UNSUPPORTED, "unknown mask");
   if (d.mask == JATTN_MASK_WINDOW) {
@@ -463,6 +466,44 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
 }
 
 void jattn_plan_destroy(jattn_plan* p) { delete p; }
+
+namespace {
+int l2norm_check(int64_t rows, int32_t D, std::initializer_list<int32_t> dtypes) {
+  if (rows < 0) return fail(JATTN_E_SHAPE, "rows must be >= 0");
+  if (D != 32 && D != 64 && D != 128) return fail(JATTN_E_SHAPE, "D must be 32, 64 or 128");
+  if (rows > (int64_t(1) << 40) / D) return fail(JATTN_E_SHAPE, "too many rows");
+  for (int32_t t : dtypes)
+    if (t != JATTN_BF16 && t != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown dtype");
+  return JATTN_OK;
+}
+}  // namespace
+
+int jattn_l2norm_fwd(const void* x, void* y, float* rnorm, int64_t rows, int32_t D, int32_t x_dtype,
+                     int32_t y_dtype, void* stream) {
+  const int c = l2norm_check(rows, D, {x_dtype, y_dtype});
+  if (c != JATTN_OK) return c;
+  if (rows == 0) return ok();
+  if (!x || !y) return fail(JATTN_E_NULL, "null x/y");
+  if (!aligned(x, 16) || !aligned(y, 16) || (rnorm && !aligned(rnorm, 4)))
+    return fail(JATTN_E_ALIGN, "x/y must be 16-byte aligned, rnorm 4-byte aligned");
+  const hipError_t e = jattn::launch_l2norm_fwd(x, y, rnorm, rows, D, x_dtype == JATTN_F32, y_dtype == JATTN_F32,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "l2norm forward launch");
+  return ok();
+}
+
+int jattn_l2norm_bwd(const void* x, const void* dy, void* dx, int64_t rows, int32_t D, int32_t x_dtype,
+                     int32_t dy_dtype, int32_t dx_dtype, void* stream) {
+  const int c = l2norm_check(rows, D, {x_dtype, dy_dtype, dx_dtype});
+  if (c != JATTN_OK) return c;
+  if (rows == 0) return ok();
+  if (!x || !dy || !dx) return fail(JATTN_E_NULL, "null x/dy/dx");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16)) return fail(JATTN_E_ALIGN, "x/dy/dx must be 16-byte aligned");
+  const hipError_t e = jattn::launch_l2norm_bwd(x, dy, dx, rows, D, x_dtype == JATTN_F32, dy_dtype == JATTN_F32,
+                                                dx_dtype == JATTN_F32, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "l2norm backward launch");
+  return ok();
+}
 
 }  // extern "C"
 

@@ -46,6 +46,7 @@ template <int D, int WKV, int WKQ>
 hipError_t dkdv2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.act == kSoftmax) return dkdv2_act<D, WKV, WKQ, kSoftmax>(a, k, grid, st);
   if (k.act == kGelu) return dkdv2_act<D, WKV, WKQ, kGelu>(a, k, grid, st);
+  if (k.act == kGeluPoly) return dkdv2_act<D, WKV, WKQ, kGeluPoly>(a, k, grid, st);
   return dkdv2_act<D, WKV, WKQ, kSilu>(a, k, grid, st);
 }
 
@@ -58,6 +59,7 @@ hipError_t JATTN_DKDV2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int
   if (k.window) {
     if (k.act == kSoftmax) return dkdv2_window<kSoftmax>(a, k, grid, st);
     if (k.act == kGelu) return dkdv2_window<kGelu>(a, k, grid, st);
+    if (k.act == kGeluPoly) return dkdv2_window<kGeluPoly>(a, k, grid, st);
     return dkdv2_window<kSilu>(a, k, grid, st);
   }
   if (k.wkv == 4) return dkdv2_shape<J_D, 4, 1>(a, k, grid, st);

@@ -28,6 +28,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSoftmax = 0;
 constexpr int kGelu = 1;
 constexpr int kSilu = 2;
+constexpr int kGeluPoly = 3;
 
 // ---------------------------------------------------------------------------
 // Sample table entry as uploaded by the host: {q0, lq, k0, lk, bias_lo,
@@ -177,13 +178,37 @@ __device__ __forceinline__ int window_first_step(int r0, int near, int step_rows
 // so that a row whose first keys are all masked stays finite.
 constexpr float kNoScore = -16384.0f;
 
-// erf-GELU and SiLU (GDPA activations) and their derivatives, fp32.
+// ALU-only GELU ("Training GEM at LLM scale", section "Generalized
+// Dot-Product Attention (GDPA)", item on the ALU-only activation): GELU's
+// tanh form 0.5 x (1 + tanh(c (x + a x^3))), c = sqrt(2/pi), a = 0.044715,
+// with tanh replaced by its Taylor polynomial through order 6,
+// t(u) = u - u^3/3 + 2 u^5/15; its derivative is a polynomial as well.
+// Meant for the bounded scores that QK-norm gives.
+constexpr float kGeluTanhC = 0.7978845608028654f;
+constexpr float kGeluTanhA = 0.044715f;
+__device__ __forceinline__ float gelu_poly_u(float x) { return kGeluTanhC * x * fmaf(kGeluTanhA, x * x, 1.0f); }
+__device__ __forceinline__ float tanh_poly(float u) {
+  const float u2 = u * u;
+  return u * fmaf(u2, fmaf(u2, 2.0f / 15.0f, -1.0f / 3.0f), 1.0f);
+}
+__device__ __forceinline__ float gelu_poly(float x) { return 0.5f * x * (1.0f + tanh_poly(gelu_poly_u(x))); }
+__device__ __forceinline__ float gelu_poly_grad(float x) {
+  const float u = gelu_poly_u(x), u2 = u * u;
+  const float dt = fmaf(u2, fmaf(u2, 2.0f / 3.0f, -1.0f), 1.0f);   // t'(u)
+  const float du = kGeluTanhC * fmaf(3.0f * kGeluTanhA, x * x, 1.0f);  // u'(x)
+  return 0.5f * (1.0f + tanh_poly(u)) + 0.5f * x * dt * du;
+}
+
+// erf-GELU, SiLU and the ALU-only GELU (GDPA activations) and their
+// derivatives, fp32.
 __device__ __forceinline__ float act_fwd(int act, float x) {
+  if (act == kGeluPoly) return gelu_poly(x);
   if (act == kGelu) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
   // SiLU: x * sigmoid(x)
   return x / (1.0f + __expf(-x));
 }
 __device__ __forceinline__ float act_grad(int act, float x) {
+  if (act == kGeluPoly) return gelu_poly_grad(x);
   if (act == kGelu) {
     const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
     const float pdf = 0.3989422804014327f * __expf(-0.5f * x * x);

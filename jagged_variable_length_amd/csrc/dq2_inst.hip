@@ -43,6 +43,7 @@ template <int WQ, int WK>
 hipError_t dq2_shape(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.act == kSoftmax) return dq2_act<WQ, WK, kSoftmax>(a, k, grid, st);
   if (k.act == kGelu) return dq2_act<WQ, WK, kGelu>(a, k, grid, st);
+  if (k.act == kGeluPoly) return dq2_act<WQ, WK, kGeluPoly>(a, k, grid, st);
   return dq2_act<WQ, WK, kSilu>(a, k, grid, st);
 }
 
@@ -55,6 +56,7 @@ hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int g
   if (k.window) {
     if (k.act == kSoftmax) return dq2_window<kSoftmax>(a, k, grid, st);
     if (k.act == kGelu) return dq2_window<kGelu>(a, k, grid, st);
+    if (k.act == kGeluPoly) return dq2_window<kGeluPoly>(a, k, grid, st);
     return dq2_window<kSilu>(a, k, grid, st);
   }
   if (k.wq == 4) return dq2_shape<4, 2>(a, k, grid, st);

@@ -29,6 +29,7 @@ hipError_t window(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st
     return one<TO, 4, 2, kSoftmax, false, false, true>(a, grid, st);
   }
   if (k.act == kGelu) return window_act<TO, kGelu>(a, k, grid, st);
+  if (k.act == kGeluPoly) return window_act<TO, kGeluPoly>(a, k, grid, st);
   return window_act<TO, kSilu>(a, k, grid, st);
 }
 template <typename TO, int WQ, int WK>
@@ -38,6 +39,7 @@ hipError_t shape(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st)
   if constexpr (WQ == 1 && J_D == 128) {
     if (k.act == kSoftmax) return one<TO, WQ, WK, kSoftmax, false, false>(a, grid, st);
     if (k.act == kGelu) return k.split ? one<TO, WQ, WK, kGelu, false, true>(a, grid, st) : one<TO, WQ, WK, kGelu, false, false>(a, grid, st);
+    if (k.act == kGeluPoly) return k.split ? one<TO, WQ, WK, kGeluPoly, false, true>(a, grid, st) : one<TO, WQ, WK, kGeluPoly, false, false>(a, grid, st);
     return k.split ? one<TO, WQ, WK, kSilu, false, true>(a, grid, st) : one<TO, WQ, WK, kSilu, false, false>(a, grid, st);
   } else {
     return shape_all<TO, WQ, WK>(a, k, grid, st);
@@ -52,6 +54,10 @@ hipError_t shape_all(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t
   if (k.act == kGelu) {
     if (k.bias) return k.split ? one<TO, WQ, WK, kGelu, true, true>(a, grid, st) : one<TO, WQ, WK, kGelu, true, false>(a, grid, st);
     return k.split ? one<TO, WQ, WK, kGelu, false, true>(a, grid, st) : one<TO, WQ, WK, kGelu, false, false>(a, grid, st);
+  }
+  if (k.act == kGeluPoly) {
+    if (k.bias) return k.split ? one<TO, WQ, WK, kGeluPoly, true, true>(a, grid, st) : one<TO, WQ, WK, kGeluPoly, true, false>(a, grid, st);
+    return k.split ? one<TO, WQ, WK, kGeluPoly, false, true>(a, grid, st) : one<TO, WQ, WK, kGeluPoly, false, false>(a, grid, st);
   }
   if (k.bias) return k.split ? one<TO, WQ, WK, kSilu, true, true>(a, grid, st) : one<TO, WQ, WK, kSilu, true, false>(a, grid, st);
   return k.split ? one<TO, WQ, WK, kSilu, false, true>(a, grid, st) : one<TO, WQ, WK, kSilu, false, false>(a, grid, st);

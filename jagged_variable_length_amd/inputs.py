@@ -26,6 +26,7 @@ import numpy as np
 ACT_SOFTMAX = "softmax"
 ACT_GELU = "gelu"
 ACT_SILU = "silu"
+ACT_GELU_POLY = "gelu_poly"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -47,6 +48,8 @@ class Workload:
     split_operands: bool
     dbias_dtype: str = "f32"
     window: Optional[tuple] = None  # sliding window (left, right), self-attention only
+    qk_norm: bool = False  # Q and K rows L2-normalised before attention (and in the backward)
+    scale: Optional[float] = None  # score scale; None = 1/sqrt(D)
 
 
 WORKLOADS = {
@@ -58,6 +61,10 @@ WORKLOADS = {
     # sliding-window self-attention over long sequences (lengths as workload 4)
     5: Workload("swa_long_w256", 64, 4, 128, "bf16", ACT_SOFTMAX, False, False, False, "bf16", "bf16", False,
                 window=(256, 256)),
+    # pooled multi-head attention shapes (as workload 3) with QK-norm and the
+    # ALU-only polynomial GELU; scale 1, so every score is a cosine in [-1, 1]
+    6: Workload("gdpa_qknorm_gelu_poly", 256, 8, 128, "bf16", ACT_GELU_POLY, False, False, False, "f32", "f32",
+                True, qk_norm=True, scale=1.0),
 }
 
 
@@ -110,7 +117,7 @@ def _lengths_from(rng, cfg):
         lq = _lognormal_lengths(rng, w.B, 500, 16, 2000)
         lk = rng.integers(16, 65, w.B).astype(np.int64)
         return lq, lk
-    if cfg == 3:
+    if cfg in (3, 6):
         lq = np.full(w.B, 32, dtype=np.int64)
         lk = _lognormal_lengths(rng, w.B, 1500, 64, 4000)
         return lq, lk

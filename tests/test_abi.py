@@ -25,7 +25,7 @@ def lib():
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "jattn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(jattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(jattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported(lib):
@@ -85,6 +85,9 @@ def _desc(**kw):
     (dict(mask=B.JATTN_MASK_WINDOW, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
      [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
     (dict(mask=B.JATTN_MASK_WINDOW, has_bias=1, want_dbias=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(act=B.JATTN_GELU_POLY, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
+     [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(act=4), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
 ])
 def test_plan_create_rejects(lib, kw, qo, ko, code):
     d = _desc(**kw)
@@ -252,3 +255,29 @@ def test_window_plans_match(lib, seed):
             assert info.flops_fwd == pytest.approx(4.0 * 3 * D * pairs, rel=1e-12)
         finally:
             B.jattn_plan_destroy(p)
+
+
+def test_l2norm_validation_never_touches_gpu(lib):
+    fake = 0x10000000
+    cases = [
+        (dict(rows=-1), B.JATTN_E_SHAPE),
+        (dict(D=48), B.JATTN_E_SHAPE),
+        (dict(xt=7), B.JATTN_E_UNSUPPORTED),
+        (dict(x=None), B.JATTN_E_NULL),
+        (dict(x=fake + 8), B.JATTN_E_ALIGN),
+        (dict(r=fake + 2), B.JATTN_E_ALIGN),
+    ]
+    for kw, code in cases:
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_l2norm_fwd(kw.get("x", fake), fake, kw.get("r", None), kw.get("rows", 10), kw.get("D", 64),
+                               kw.get("xt", B.JATTN_BF16), B.JATTN_BF16, None)
+        assert e.value.code == code, kw
+    with pytest.raises(B.JattnError) as e:
+        B.jattn_l2norm_bwd(fake, None, fake, 10, 64, B.JATTN_BF16, B.JATTN_F32, B.JATTN_F32, None)
+    assert e.value.code == B.JATTN_E_NULL
+    with pytest.raises(B.JattnError) as e:
+        B.jattn_l2norm_bwd(fake, fake, fake, 10, 64, B.JATTN_BF16, B.JATTN_F32, 5, None)
+    assert e.value.code == B.JATTN_E_UNSUPPORTED
+    # zero rows: a no-op that touches no pointer
+    B.jattn_l2norm_fwd(None, None, None, 0, 64, B.JATTN_BF16, B.JATTN_BF16, None)
+    B.jattn_l2norm_bwd(None, None, None, 0, 64, B.JATTN_BF16, B.JATTN_BF16, B.JATTN_BF16, None)
