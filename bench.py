@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..6 (1 = headline)")
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..7 (1 = headline)")
     ap.add_argument("--order", default="zigzag", help="unit order across workers (the zigzag deal by default)")
     ap.add_argument("--workers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -208,6 +208,8 @@ def cpu_baseline(w, inp, budget_s):
     scale = 1.0 / np.sqrt(w.D) if w.scale is None else w.scale
     if w.qk_norm:
         return _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores)
+    if w.rope:
+        return _cpu_baseline_rope(w, inp, q, k, v, do, scale, budget_s, cores)
     # warm-up on a small sample
     lq, lk = inp.lq, inp.lk
     order = list(np.argsort(lq, kind="stable")) if w.window is not None else list(range(inp.B))
@@ -265,6 +267,31 @@ def _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores):
                       f"float64, {dt:.1f} s"}
 
 
+def _cpu_baseline_rope(w, inp, q, k, v, do, scale, budget_s, cores):
+    """RoPE, block attention and both backwards per sample, in float64."""
+    from oracle import attention as ora
+    from oracle import rope
+    flops, n = 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(inp.B):
+        s_ = slice(int(inp.q_offsets[b]), int(inp.q_offsets[b + 1]))
+        off = np.array([0, s_.stop - s_.start])
+        qr, kr = rope.forward(q[s_], off), rope.forward(k[s_], off)
+        ora.forward(qr, kr, v[s_], off, off, scale=scale, block_diagonal=True)
+        dqr, dkr, _, _ = ora.backward(qr, kr, v[s_], do[s_], off, off, scale=scale, block_diagonal=True)
+        rope.backward(dqr, off)
+        rope.backward(dkr, off)
+        L = int(inp.lq[b])
+        flops += 3.5 * 4.0 * w.H * w.D * sum(min(64, L - s0) ** 2 for s0 in range(0, L, 64))
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), RoPE + block attention, fwd+bwd in "
+                      f"float64, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -291,7 +318,7 @@ def main():
                            has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
                            num_workers=args.workers, dbias_dtype=w.dbias_dtype, window=w.window,
-                           scale=w.scale)
+                           scale=w.scale, rope=w.rope)
     t0 = time.perf_counter()
     plan_ms = None
     op.upload()
@@ -412,7 +439,8 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} D={w.D} {w.dtype} act={w.act}"
                                f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}"
                                f"{f' window={w.window}' if w.window else ''}"
-                               f"{f' qk-norm scale={w.scale}' if w.qk_norm else ''}",
+                               f"{f' qk-norm scale={w.scale}' if w.qk_norm else ''}"
+                               f"{' rope' if w.rope else ''}",
                    "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk, "seed": cfg,
                    "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),
                    "order": args.order, "out_dtype": w.out_dtype, "grad_dtype": w.grad_dtype,

@@ -121,6 +121,15 @@ typedef struct {
   int32_t window_left;  /* JATTN_MASK_WINDOW: keys before the query it sees (>= 0) */
   int32_t window_right; /* JATTN_MASK_WINDOW: keys after the query it sees (>= 0);
                            both are ignored for other masks */
+  int32_t rope;         /* 0/1, JATTN_MASK_BLOCKDIAG64 only: rotary position
+                           embedding of Q and K fused into the block kernels
+                           (section "BlockAttention": RoPE backward fused into
+                           the attention epilogue).  Rotate-half pairs
+                           (j, j + D/2) at position m (token index inside the
+                           sample) turn by m * rope_base^(-2j/D); q, k stay
+                           un-rotated in memory and dq, dk are the gradients
+                           with respect to them. */
+  float rope_base;      /* <= 0 selects 10000 */
 } jattn_desc;
 
 /* Per-kernel plan figures.  tile_rows: rows of the unit's own tile (q rows

@@ -35,7 +35,8 @@ class JaggedAttention:
                  in_dtype: str = "bf16", out_dtype: Optional[str] = None,
                  grad_dtype: Optional[str] = None, split_operands: bool = False,
                  order: str = "zigzag", num_workers: int = 0, scale: Optional[float] = None,
-                 dbias_dtype: Optional[str] = None, window: Optional[tuple] = None, device="cuda"):
+                 dbias_dtype: Optional[str] = None, window: Optional[tuple] = None, rope: bool = False,
+                 rope_base: float = 0.0, device="cuda"):
         q_offsets = np.asarray(q_offsets, dtype=np.int64)
         kv_offsets = np.asarray(kv_offsets, dtype=np.int64)
         self.B = len(q_offsets) - 1
@@ -57,6 +58,8 @@ class JaggedAttention:
         if self.window is not None:
             d.mask = _b.JATTN_MASK_WINDOW
             d.window_left, d.window_right = self.window
+        self.rope = bool(rope)
+        d.rope, d.rope_base = int(rope), float(rope_base)
         d.has_bias, d.want_dbias = int(has_bias), int(want_dbias)
         d.in_dtype, d.out_dtype, d.grad_dtype = _DT[in_dtype], _DT[self.out_dtype], _DT[self.grad_dtype]
         d.split_operands = int(split_operands)

@@ -44,7 +44,7 @@ class jattn_desc(ctypes.Structure):
                 ("grad_dtype", ctypes.c_int32), ("split_operands", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("dbias_dtype", ctypes.c_int32), ("window_left", ctypes.c_int32),
-                ("window_right", ctypes.c_int32)]
+                ("window_right", ctypes.c_int32), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float)]
 
 
 class jattn_kernel_plan(ctypes.Structure):

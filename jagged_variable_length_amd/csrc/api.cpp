@@ -28,6 +28,7 @@ struct jattn_plan {
   std::vector<int32_t> image;  // uploaded plan (int32 words)
   int64_t off_samples = 0, off_fwd_u = 0, off_fwd_o = 0, off_dkdv_u = 0, off_dkdv_o = 0;
   int64_t off_dq_u = 0, off_dq_o = 0, off_blk_u = 0, off_blk_o = 0;  // in int32 words
+  int64_t off_theta = -1;  // RoPE theta table (fp64), in int32 words; -1 without RoPE
   int64_t plan_bytes = 0, di_off = 0, lse2_off = 0, workspace_bytes = 0;
 };
 
@@ -138,6 +139,11 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     return fail(JATTN_E_UNSUPPORTED, "block-diagonal mode supports softmax without bias");
   if (d.mask == JATTN_MASK_BLOCKDIAG64 && d.in_dtype != JATTN_BF16)
     return fail(JATTN_E_UNSUPPORTED, "block-diagonal mode needs bf16 inputs");
+  if (d.rope != 0 && d.rope != 1) return fail(JATTN_E_ARG, "rope must be 0 or 1");
+  if (d.rope && d.mask != JATTN_MASK_BLOCKDIAG64)
+    return fail(JATTN_E_UNSUPPORTED, "RoPE is fused into the block-diagonal kernels only");
+  if (d.rope && !(d.rope_base <= 0.f || (d.rope_base > 1.f && !isinf(d.rope_base))))
+    return fail(JATTN_E_ARG, "rope_base must be > 1 (or <= 0 for the default)");
   if (d.mask == JATTN_MASK_BLOCKDIAG64 && (d.num_workers % 2) != 0)
     return fail(JATTN_E_ARG, "block-diagonal mode needs an even num_workers (two per workgroup)");
   if (d.order < JATTN_HEAVY_FIRST || d.order > JATTN_LPT) return fail(JATTN_E_ARG, "unknown order");
@@ -255,6 +261,19 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   append(p->image, p->dkdv, &p->off_dkdv_u, &p->off_dkdv_o);
   append(p->image, p->dq, &p->off_dq_u, &p->off_dq_o);
   append(p->image, p->block, &p->off_blk_u, &p->off_blk_o);
+  if (d.rope) {
+    // theta_j = base^(-2j/D), j < D/2, as fp64 words
+    const double base = d.rope_base > 0.f ? (double)d.rope_base : 10000.0;
+    p->image.resize((size_t)align_up((int64_t)p->image.size(), 4), 0);
+    p->off_theta = (int64_t)p->image.size();
+    for (int j = 0; j < d.D / 2; ++j) {
+      const double th = pow(base, -2.0 * j / d.D);
+      int32_t w[2];
+      memcpy(w, &th, 8);
+      p->image.push_back(w[0]);
+      p->image.push_back(w[1]);
+    }
+  }
   p->plan_bytes = (int64_t)p->image.size() * 4;
   p->di_off = align_up(p->plan_bytes, 256);
   p->lse2_off = p->di_off + align_up(p->Tq * d.H * 4, 256);
@@ -360,6 +379,7 @@ int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
     a.lse = nullptr;  // no row statistics leave a block
     a.units = ws_ptr(workspace, p->off_blk_u);
     a.worker_off = ws_ptr(workspace, p->off_blk_o);
+    if (p->off_theta >= 0) a.rope_theta = reinterpret_cast<const double*>(ws_ptr(workspace, p->off_theta));
     e = jattn::launch_block_fwd(a, sel, p->block.num_workers / 2, st);
   } else {
     e = jattn::launch_fwd(a, sel, p->fwd.num_workers, st);
@@ -418,6 +438,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
     a.units = ws_ptr(workspace, p->off_blk_u);
     a.worker_off = ws_ptr(workspace, p->off_blk_o);
     a.samples = ws_ptr(workspace, p->off_samples);
+    if (p->off_theta >= 0) a.rope_theta = reinterpret_cast<const double*>(ws_ptr(workspace, p->off_theta));
     a.H = p->H;
     a.scale = p->scale;
     a.scale_log2 = p->scale * 1.4426950408889634f;

@@ -18,6 +18,16 @@
 //           phase-1 row statistics, dV = P^T dO, dK = dS^T Q.
 // Operands that are contracted along rows (V^T, K^T, Q^T, dO^T) are read
 // from the row-major LDS tiles with ds_read_b64_tr_b16.
+//
+// Rotary position embedding (ROPE; same section: the RoPE backward is fused
+// into the block-attention epilogue and the gradients stay in fp32
+// registers).  Rotate-half pairs (j, j + D/2) at position m (token index in
+// the sample) turn by m * theta_j, theta_j = base^(-2j/D) (fp64 table in the
+// plan).  The forward rotates Q in registers and K in LDS after they land;
+// the backward rotates the Q and K tiles in LDS once, and applies the
+// transposed rotation to dQ and dK in the accumulator registers before the
+// store.  The angle is reduced to [-pi, pi] in fp64, then sine and cosine
+// are taken in fp32.
 #pragma once
 #include "common.hpp"
 #include "fwd_impl.hpp"
@@ -66,6 +76,69 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+__device__ __forceinline__ void wait_lds() {
+  // s_waitcnt lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// theta_j from the plan's table, through the scalar cache (j is uniform)
+__device__ __forceinline__ double rope_theta(const double* t, int j) {
+  return ((__attribute__((address_space(4))) const double*)t)[j];
+}
+
+// cos and sin of m * theta: the angle is formed and reduced to [-pi, pi] in
+// fp64 (positions reach 2^25, where an fp32 angle would be off by radians)
+__device__ __forceinline__ void rope_cs(int m, double theta, float& c, float& s) {
+  constexpr double kTwoPi = 6.283185307179586;
+  const double a = (double)m * theta;
+  const float r = (float)fma(-rint(a * (1.0 / kTwoPi)), kTwoPi, a);
+  __sincosf(r, &s, &c);
+}
+
+// Rotate rows of a 64-row LDS tile in place: this lane takes row `row` and
+// the chunk pairs (cc, cc + CPR/2) for cc in [c0, c1); position = m.
+template <int D>
+__device__ __forceinline__ void rope_rows_lds(char* tile, const double* theta, int row, int m, int c0, int c1) {
+  using T = Tile<D>;
+  for (int cc = c0; cc < c1; ++cc) {
+    bf16x8* p1 = reinterpret_cast<bf16x8*>(tile + T::off(row, cc * 8));
+    bf16x8* p2 = reinterpret_cast<bf16x8*>(tile + T::off(row, cc * 8 + D / 2));
+    bf16x8 x1 = *p1, x2 = *p2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c, s;
+      rope_cs(m, rope_theta(theta, cc * 8 + e), c, s);
+      const float a1 = (float)x1[e], a2 = (float)x2[e];
+      x1[e] = (bf16)(a1 * c - a2 * s);
+      x2[e] = (bf16)(a2 * c + a1 * s);
+    }
+    *p1 = x1;
+    *p2 = x2;
+  }
+}
+
+// Transposed rotation of a gradient row held in accumulator order: slot i of
+// block d is column d*32 + acc_row(i, g).  Blocks d and d + ND/2 pair up; with
+// one block (D = 32) the pairs are slots i and i + 8 (columns c, c + 16).
+template <int ND>
+__device__ __forceinline__ void rope_back_acc(f32x16* acc, const double* theta, int m, int g) {
+  constexpr int NB = ND > 1 ? ND / 2 : 1;   // blocks holding first halves
+  constexpr int NI = ND > 1 ? 16 : 8;       // their slots holding first halves
+#pragma unroll
+  for (int d = 0; d < NB; ++d)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j0 = d * 32 + (i >> 2) * 8 + (i & 3);  // column for g = 0; g = 1 adds 4
+      const double th = g ? rope_theta(theta, j0 + 4) : rope_theta(theta, j0);
+      float c, s;
+      rope_cs(m, th, c, s);
+      constexpr int D2 = ND > 1 ? ND / 2 : 0, I2 = ND > 1 ? 0 : 8;  // partner: block d + D2, slot i + I2
+      const float a1 = acc[d][i], a2 = acc[d + D2][i + I2];
+      acc[d][i] = a1 * c + a2 * s;
+      acc[d + D2][i + I2] = a2 * c - a1 * s;
+    }
+}
+
 // bf16 fragment from 8 consecutive accumulator slots
 __device__ __forceinline__ bf16x8 pack8_from(const f32x16& v, int off) {
   bf16x8 r;
@@ -100,7 +173,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int blk, int st, int
 // ---------------------------------------------------------------------------
 // forward: one wave = one 64 x 64 block
 // ---------------------------------------------------------------------------
-template <typename TO, int D>
+template <typename TO, int D, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
   using T = Tile<D>;
   constexpr int NKK = D / 16, ND = D / 32;
@@ -135,8 +208,30 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         qf[qb][kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)((qb * 32 + l32) * HD + kk * 16 + g * 8) * 2));
+    if constexpr (ROPE) {
+      // Q in registers: element e of fragment kk is column kk*16 + g*8 + e
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < NKK / 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double th = g ? rope_theta(a.rope_theta, kk * 16 + 8 + e) : rope_theta(a.rope_theta, kk * 16 + e);
+            float c, s;
+            rope_cs(row0 + qb * 32 + l32, th, c, s);
+            const float x1 = (float)qf[qb][kk][e], x2 = (float)qf[qb][kk + NKK / 2][e];
+            qf[qb][kk][e] = (bf16)(x1 * c - x2 * s);
+            qf[qb][kk + NKK / 2][e] = (bf16)(x2 * c + x1 * s);
+          }
+    }
     wait_vmem();
     __builtin_amdgcn_wave_barrier();
+    if constexpr (ROPE) {
+      // K in this wave's LDS tile: lane = row (rows past the sample end are zero)
+      rope_rows_lds<D>(kt, a.rope_theta, lane, row0 + lane, 0, T::CPR / 2);
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+    }
 
     // S^T[kb][qb]
     f32x16 sacc[2][2];
@@ -204,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // backward: a wave pair per block, two pairs per workgroup in lockstep
 // ---------------------------------------------------------------------------
-template <typename TG, int D>
+template <typename TG, int D, bool ROPE = false>
 __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
   using T = Tile<D>;
   constexpr int NKK = D / 16, ND = D / 32;
@@ -229,13 +324,13 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
   for (int k = 0; k < rounds; ++k) {
     const int u = u0 + k;
     const bool active = u < u1;
-    int r = 0;
+    int r = 0, row0 = 0;
     int64_t qbase = 0, kbase = 0;
     if (active) {
       const i32x4 unit = load_unit(a.units, u);
       const int b = unit[0], h = unit[1], t = unit[2];
       const Sample s = load_sample(a.samples, b);
-      const int row0 = t * 64;
+      row0 = t * 64;
       r = min(64, s.lq - row0);
       qbase = ((int64_t)(s.q0 + row0) * a.H + h) * D;
       kbase = ((int64_t)(s.k0 + row0) * a.H + h) * D;
@@ -251,6 +346,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
     }
     wait_vmem();
     __syncthreads();
+    if constexpr (ROPE) {
+      // rotate the Q and K tiles once: the pair's 128 lanes take half a row each
+      if (active) {
+        const int lr = (w2 * 64 + lane) >> 1, half = lane & 1;
+        constexpr int CQ = T::CPR / 4;  // chunk pairs per half row
+        rope_rows_lds<D>(qt, a.rope_theta, lr, row0 + lr, half * CQ, half * CQ + CQ);
+        rope_rows_lds<D>(kt, a.rope_theta, lr, row0 + lr, half * CQ, half * CQ + CQ);
+      }
+      wait_lds();
+      __syncthreads();
+    }
 
     const int npad = 64 - r;
     // ---- phase 1: lane = query row (w2*32 + l32) ----
@@ -323,6 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
           for (int d = 0; d < ND; ++d) dqacc[d] = Elem<bf16>::mma(tr_frag<D>(kt, kb, st, d * 32, lane), df, dqacc[d]);
         }
       const int row = w2 * 32 + l32;
+      if constexpr (ROPE) rope_back_acc<ND>(dqacc, a.rope_theta, row0 + row, g);
       if (row < r) {
         TG* grow = reinterpret_cast<TG*>(a.dq) + qbase + (int64_t)row * HD;
 #pragma unroll
@@ -376,6 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
         }
       }
       const int row = w2 * 32 + l32;
+      if constexpr (ROPE) rope_back_acc<ND>(dkacc, a.rope_theta, row0 + row, g);
       if (row < r) {
         TG* krp = reinterpret_cast<TG*>(a.dk) + kbase + (int64_t)row * HD;
         TG* vrp = reinterpret_cast<TG*>(a.dv) + kbase + (int64_t)row * HD;

@@ -28,6 +28,7 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
   int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
   int win_l, win_r;    // sliding window: query i sees keys i - win_l .. i + win_r
+  const double* rope_theta;  // block mode with RoPE: theta_j, j < D/2 (else null)
 };
 
 struct DiArgs {
@@ -60,6 +61,7 @@ struct BwdArgs {
   float scale_log2;
   int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
   int win_l, win_r;    // sliding window: query i sees keys i - win_l .. i + win_r
+  const double* rope_theta;  // block mode with RoPE: theta_j, j < D/2 (else null)
 };
 
 // Which template instance to run.

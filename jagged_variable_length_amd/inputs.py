@@ -50,6 +50,7 @@ class Workload:
     window: Optional[tuple] = None  # sliding window (left, right), self-attention only
     qk_norm: bool = False  # Q and K rows L2-normalised before attention (and in the backward)
     scale: Optional[float] = None  # score scale; None = 1/sqrt(D)
+    rope: bool = False  # block mode: rotary embedding of Q and K fused into the kernels
 
 
 WORKLOADS = {
@@ -65,6 +66,9 @@ WORKLOADS = {
     # ALU-only polynomial GELU; scale 1, so every score is a cosine in [-1, 1]
     6: Workload("gdpa_qknorm_gelu_poly", 256, 8, 128, "bf16", ACT_GELU_POLY, False, False, False, "f32", "f32",
                 True, qk_norm=True, scale=1.0),
+    # BlockAttention (workload 4's shapes) with the rotary embedding fused in
+    7: Workload("block_attention_64_rope", 64, 4, 128, "bf16", ACT_SOFTMAX, True, False, False, "bf16", "bf16",
+                False, rope=True),
 }
 
 
@@ -121,7 +125,7 @@ def _lengths_from(rng, cfg):
         lq = np.full(w.B, 32, dtype=np.int64)
         lk = _lognormal_lengths(rng, w.B, 1500, 64, 4000)
         return lq, lk
-    if cfg in (4, 5):
+    if cfg in (4, 5, 7):
         lq = rng.integers(2048, 16385, w.B).astype(np.int64)
         return lq, lq.copy()
     raise ValueError(f"unknown workload {cfg}")

@@ -56,6 +56,7 @@ def _desc(**kw):
     d.order = kw.get("order", B.JATTN_HEAVY_FIRST)
     d.num_workers = kw.get("num_workers", 0)
     d.window_left, d.window_right = kw.get("window", (0, 0))
+    d.rope, d.rope_base = kw.get("rope", 0), kw.get("rope_base", 0.0)
     return d
 
 
@@ -88,6 +89,9 @@ def _desc(**kw):
     (dict(act=B.JATTN_GELU_POLY, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32),
      [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
     (dict(act=4), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),
+    (dict(rope=1), [0, 3, 5], [0, 3, 5], B.JATTN_E_UNSUPPORTED),  # RoPE needs block mode
+    (dict(rope=2, mask=B.JATTN_MASK_BLOCKDIAG64), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
+    (dict(rope=1, rope_base=0.5, mask=B.JATTN_MASK_BLOCKDIAG64), [0, 3, 5], [0, 3, 5], B.JATTN_E_ARG),
 ])
 def test_plan_create_rejects(lib, kw, qo, ko, code):
     d = _desc(**kw)
@@ -281,3 +285,17 @@ def test_l2norm_validation_never_touches_gpu(lib):
     # zero rows: a no-op that touches no pointer
     B.jattn_l2norm_fwd(None, None, None, 0, 64, B.JATTN_BF16, B.JATTN_BF16, None)
     B.jattn_l2norm_bwd(None, None, None, 0, 64, B.JATTN_BF16, B.JATTN_BF16, B.JATTN_BF16, None)
+
+
+def test_rope_plan_grows_by_theta_table(lib):
+    """Block plans with RoPE carry D/2 fp64 angles in their uploaded image."""
+    L = [70, 129]
+    off = gen.offsets_from_lengths(L)
+    sizes = []
+    for rope in (0, 1):
+        p = B.jattn_plan_create(_desc(B=2, H=2, D=128, mask=B.JATTN_MASK_BLOCKDIAG64, rope=rope), off, off)
+        try:
+            sizes.append(B.jattn_plan_info(p).workspace_bytes)
+        finally:
+            B.jattn_plan_destroy(p)
+    assert sizes[1] - sizes[0] in range(64 * 8, 64 * 8 + 512)
