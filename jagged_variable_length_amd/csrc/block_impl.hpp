@@ -81,9 +81,13 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(0xC07F);
 }
 
-// theta_j from the plan's table, through the scalar cache (j is uniform)
-__device__ __forceinline__ double rope_theta(const double* t, int j) {
-  return ((__attribute__((address_space(4))) const double*)t)[j];
+// theta_j from the workgroup's LDS copy of the plan's table
+__device__ __forceinline__ double rope_theta(const double* t, int j) { return t[j]; }
+
+// copy the D/2 angles of the plan's table into LDS (before a barrier)
+template <int D>
+__device__ __forceinline__ void stage_theta(double* dst, const double* src) {
+  for (int j = threadIdx.x; j < D / 2; j += kThreads) dst[j] = src[j];
 }
 
 // cos and sin of m * theta: the angle is formed and reduced to [-pi, pi] in
@@ -95,12 +99,13 @@ __device__ __forceinline__ void rope_cs(int m, double theta, float& c, float& s)
   __sincosf(r, &s, &c);
 }
 
-// Rotate rows of a 64-row LDS tile in place: this lane takes row `row` and
-// the chunk pairs (cc, cc + CPR/2) for cc in [c0, c1); position = m.
+// Rotate one row of a 64-row LDS tile in place (this lane's row `row`, at
+// position m): chunk pairs (cc, cc + CPR/2).
 template <int D>
-__device__ __forceinline__ void rope_rows_lds(char* tile, const double* theta, int row, int m, int c0, int c1) {
+__device__ __forceinline__ void rope_rows_lds(char* tile, const double* theta, int row, int m) {
   using T = Tile<D>;
-  for (int cc = c0; cc < c1; ++cc) {
+#pragma unroll 2
+  for (int cc = 0; cc < T::CPR / 2; ++cc) {
     bf16x8* p1 = reinterpret_cast<bf16x8*>(tile + T::off(row, cc * 8));
     bf16x8* p2 = reinterpret_cast<bf16x8*>(tile + T::off(row, cc * 8 + D / 2));
     bf16x8 x1 = *p1, x2 = *p2;
@@ -117,22 +122,51 @@ __device__ __forceinline__ void rope_rows_lds(char* tile, const double* theta, i
   }
 }
 
+// Backward angles of one lane: the lane's row (query in phase 1, key in
+// phase 2: the same position m) and the pair columns
+//     j(n) = (n / 4) * 8 + 4 g + n % 4,   n < D/4,
+// which are exactly the first-half columns of the lane's accumulator slots
+// (slot i of block d is column d*32 + acc_row(i, g), i.e. n = d*16 + i).
+template <int D>
+__device__ __forceinline__ void rope_lane_angles(const double* theta, int m, int g, float* rc, float* rs) {
+#pragma unroll
+  for (int n = 0; n < D / 4; ++n) rope_cs(m, rope_theta(theta, (n >> 2) * 8 + g * 4 + (n & 3)), rc[n], rs[n]);
+}
+
+// Rotate the lane's columns j(n) (and j(n) + D/2) of row `row` of an LDS tile.
+template <int D>
+__device__ __forceinline__ void rope_lane_lds(char* tile, int row, int g, const float* rc, const float* rs) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) {
+    bf16x4* p1 = reinterpret_cast<bf16x4*>(tile + T::off(row, q * 8 + g * 4));
+    bf16x4* p2 = reinterpret_cast<bf16x4*>(tile + T::off(row, q * 8 + g * 4 + D / 2));
+    bf16x4 x1 = *p1, x2 = *p2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = rc[q * 4 + e], s = rs[q * 4 + e];
+      const float a1 = (float)x1[e], a2 = (float)x2[e];
+      x1[e] = (bf16)(a1 * c - a2 * s);
+      x2[e] = (bf16)(a2 * c + a1 * s);
+    }
+    *p1 = x1;
+    *p2 = x2;
+  }
+}
+
 // Transposed rotation of a gradient row held in accumulator order: slot i of
-// block d is column d*32 + acc_row(i, g).  Blocks d and d + ND/2 pair up; with
-// one block (D = 32) the pairs are slots i and i + 8 (columns c, c + 16).
+// block d (n = d*16 + i) pairs with block d + ND/2; with one block (D = 32)
+// the pairs are slots i and i + 8 (columns c, c + 16).
 template <int ND>
-__device__ __forceinline__ void rope_back_acc(f32x16* acc, const double* theta, int m, int g) {
+__device__ __forceinline__ void rope_back_acc(f32x16* acc, const float* rc, const float* rs) {
   constexpr int NB = ND > 1 ? ND / 2 : 1;   // blocks holding first halves
   constexpr int NI = ND > 1 ? 16 : 8;       // their slots holding first halves
+  constexpr int D2 = ND > 1 ? ND / 2 : 0, I2 = ND > 1 ? 0 : 8;  // partner: block d + D2, slot i + I2
 #pragma unroll
   for (int d = 0; d < NB; ++d)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int j0 = d * 32 + (i >> 2) * 8 + (i & 3);  // column for g = 0; g = 1 adds 4
-      const double th = g ? rope_theta(theta, j0 + 4) : rope_theta(theta, j0);
-      float c, s;
-      rope_cs(m, th, c, s);
-      constexpr int D2 = ND > 1 ? ND / 2 : 0, I2 = ND > 1 ? 0 : 8;  // partner: block d + D2, slot i + I2
+      const float c = rc[d * 16 + i], s = rs[d * 16 + i];
       const float a1 = acc[d][i], a2 = acc[d + D2][i + I2];
       acc[d][i] = a1 * c + a2 * s;
       acc[d + D2][i + I2] = a2 * c - a1 * s;
@@ -178,8 +212,13 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
   using T = Tile<D>;
   constexpr int NKK = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * T::BYTES];
+  __shared__ double theta_s[ROPE ? D / 2 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g = lane >> 5;
+  if constexpr (ROPE) {
+    stage_theta<D>(theta_s, a.rope_theta);
+    __syncthreads();
+  }
   char* kt = smem + wave * 2 * T::BYTES;
   char* vt = kt + T::BYTES;
   // two waves share one worker (wave pair) and take alternate units of it
@@ -216,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
         for (int kk = 0; kk < NKK / 2; ++kk)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const double th = g ? rope_theta(a.rope_theta, kk * 16 + 8 + e) : rope_theta(a.rope_theta, kk * 16 + e);
+            const double th = rope_theta(theta_s, kk * 16 + g * 8 + e);
             float c, s;
             rope_cs(row0 + qb * 32 + l32, th, c, s);
             const float x1 = (float)qf[qb][kk][e], x2 = (float)qf[qb][kk + NKK / 2][e];
@@ -228,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_wave_barrier();
     if constexpr (ROPE) {
       // K in this wave's LDS tile: lane = row (rows past the sample end are zero)
-      rope_rows_lds<D>(kt, a.rope_theta, lane, row0 + lane, 0, T::CPR / 2);
+      rope_rows_lds<D>(kt, theta_s, lane, row0 + lane);
       wait_lds();
       __builtin_amdgcn_wave_barrier();
     }
@@ -305,6 +344,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
   constexpr int NKK = D / 16, ND = D / 32;
   constexpr int PAIR_BYTES = 4 * T::BYTES + 2 * 64 * 4;
   __shared__ __attribute__((aligned(1024))) char smem[2 * PAIR_BYTES];
+  __shared__ double theta_s[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) {
+    stage_theta<D>(theta_s, a.rope_theta);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int pair = wave >> 1, w2 = wave & 1;
@@ -344,15 +388,19 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
       load_tile_async<D>(vt, rv, 0, HD, lane, w2, 2);
       load_tile_async<D>(ot, ro, 0, HD, lane, w2, 2);
     }
+    // the lane's angles (its row w2*32 + l32 is a query in phase 1 and a key
+    // in phase 2, at one position), computed while the tiles are in flight,
+    // rotate its share of the Q and K tiles once, then the dQ and dK rows in
+    // the epilogues
+    float rc[ROPE ? D / 4 : 1], rs[ROPE ? D / 4 : 1];
+    if constexpr (ROPE)
+      if (active) rope_lane_angles<D>(theta_s, row0 + w2 * 32 + l32, g, rc, rs);
     wait_vmem();
     __syncthreads();
     if constexpr (ROPE) {
-      // rotate the Q and K tiles once: the pair's 128 lanes take half a row each
       if (active) {
-        const int lr = (w2 * 64 + lane) >> 1, half = lane & 1;
-        constexpr int CQ = T::CPR / 4;  // chunk pairs per half row
-        rope_rows_lds<D>(qt, a.rope_theta, lr, row0 + lr, half * CQ, half * CQ + CQ);
-        rope_rows_lds<D>(kt, a.rope_theta, lr, row0 + lr, half * CQ, half * CQ + CQ);
+        rope_lane_lds<D>(qt, w2 * 32 + l32, g, rc, rs);
+        rope_lane_lds<D>(kt, w2 * 32 + l32, g, rc, rs);
       }
       wait_lds();
       __syncthreads();
@@ -429,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
           for (int d = 0; d < ND; ++d) dqacc[d] = Elem<bf16>::mma(tr_frag<D>(kt, kb, st, d * 32, lane), df, dqacc[d]);
         }
       const int row = w2 * 32 + l32;
-      if constexpr (ROPE) rope_back_acc<ND>(dqacc, a.rope_theta, row0 + row, g);
+      if constexpr (ROPE) rope_back_acc<ND>(dqacc, rc, rs);
       if (row < r) {
         TG* grow = reinterpret_cast<TG*>(a.dq) + qbase + (int64_t)row * HD;
 #pragma unroll
@@ -483,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
         }
       }
       const int row = w2 * 32 + l32;
-      if constexpr (ROPE) rope_back_acc<ND>(dkacc, a.rope_theta, row0 + row, g);
+      if constexpr (ROPE) rope_back_acc<ND>(dkacc, rc, rs);
       if (row < r) {
         TG* krp = reinterpret_cast<TG*>(a.dk) + kbase + (int64_t)row * HD;
         TG* vrp = reinterpret_cast<TG*>(a.dv) + kbase + (int64_t)row * HD;
