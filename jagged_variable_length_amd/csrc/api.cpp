@@ -239,10 +239,18 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     p->dq_wq = (n_q > 0 && sum_lq <= 48 * n_q) ? 1 : 4;
     // nor has the bf16 short-query dQ kernel
     if (d.in_dtype == JATTN_BF16 && d.D == 128 && d.has_bias) p->dq_wq = 4;
-    // the windowed kernels exist for 128-row query tiles and 128-key units
+    // bf16 long queries: 8 query groups of 32 rows over one 32-key block per
+    // step (no key split, so no partials to combine); the windowed kernels
+    // keep 4 query groups x 2 key halves (128-row tiles visit fewer keys
+    // outside a window); fp32 inputs use 128-row tiles with 64-key steps
+    if (d.in_dtype == JATTN_BF16) {
+      if (p->fwd_wq == 4) p->fwd_wq = 8;
+      if (p->dq_wq == 4) p->dq_wq = 8;
+    }
     if (d.mask == JATTN_MASK_WINDOW) p->fwd_wq = p->dq_wq = 4;
-    const int fwd_tile = 32 * p->fwd_wq, fwd_step = p->fwd_wq == 4 ? 64 : 128;
-    const int dq_tile = 32 * p->dq_wq, dq_step = p->dq_wq == 4 ? 64 : 128;
+    auto step_of = [](int wq) { return wq == 8 ? 32 : wq == 4 ? 64 : 128; };
+    const int fwd_tile = 32 * p->fwd_wq, fwd_step = step_of(p->fwd_wq);
+    const int dq_tile = 32 * p->dq_wq, dq_step = step_of(p->dq_wq);
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
     // the bf16 dK/dV kernel keeps three or four step stages in LDS: 128-query

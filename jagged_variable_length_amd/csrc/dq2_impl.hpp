@@ -51,7 +51,7 @@ struct Dq2Shape {
   static constexpr int COMB_PER_D = (WK - 1) * WQ * 32 * 32 * 4;
   static constexpr int COMB = COMB_PER_D * ND;
   static constexpr bool COMB_IN_STAGE = WK > 1 && 2 * STAGE + COMB > 160 * 1024;
-  static constexpr int DP_FIT = STAGE / COMB_PER_D;
+  static constexpr int DP_FIT = WK > 1 ? STAGE / COMB_PER_D : ND;
   static_assert(!COMB_IN_STAGE || DP_FIT >= 1, "combine pass does not fit a stage");
   static constexpr int DP = !COMB_IN_STAGE || DP_FIT >= ND ? ND : (DP_FIT >= 2 && ND % 2 == 0 ? 2 : 1);
   static constexpr int SMEM = 2 * STAGE + (WK > 1 && !COMB_IN_STAGE ? COMB : 0);

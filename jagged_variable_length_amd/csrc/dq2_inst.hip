@@ -59,7 +59,8 @@ hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int g
     if (k.act == kGeluPoly) return dq2_window<kGeluPoly>(a, k, grid, st);
     return dq2_window<kSilu>(a, k, grid, st);
   }
-  if (k.wq == 4) return dq2_shape<4, 2>(a, k, grid, st);
+  if (k.wq == 8) return dq2_shape<8, 1>(a, k, grid, st);
+  if (k.wq != 1) return hipErrorInvalidValue;  // 4 x 2 serves the windowed instances only
   return dq2_shape<1, 4>(a, k, grid, st);
 }
 

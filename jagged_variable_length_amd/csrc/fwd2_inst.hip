@@ -65,9 +65,11 @@ hipError_t shape_all(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t
 template <typename TO>
 hipError_t dispatch(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.window) return window<TO>(a, k, grid, st);
-  // 4 query groups x 2 key halves (64-key steps), or 1 query group x 4 key
-  // quarters (128-key steps) for short queries
-  if (k.wq == 4) return shape<TO, 4, 2>(a, k, grid, st);
+  // 8 query groups over one 32-key block per step, or 1 query group x 4 key
+  // quarters (128-key steps) for short queries (4 x 2 serves the windowed
+  // instances above)
+  if (k.wq == 8) return shape<TO, 8, 1>(a, k, grid, st);
+  if (k.wq != 1) return hipErrorInvalidValue;
   if constexpr (J_D == 128) {
     // short queries with bias at D = 128 do not fit the LDS budget; the
     // planner never selects that combination

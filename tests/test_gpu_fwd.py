@@ -87,7 +87,7 @@ def test_fwd_short_query_bias_d128_uses_regular_shape():
     say("case: 32-row queries with bias at D=128 (regular shape)")
     inp = gen.make_custom([32, 20, 32], [700, 9, 64], 2, 128, "bf16", seed=7, bias=True)
     op, o, lse = _run_fwd(inp, bias=True)
-    assert op.info.fwd.tile_rows == 128
+    assert op.info.fwd.tile_rows == 256
     _compare(inp, op, o, lse)
 
 
