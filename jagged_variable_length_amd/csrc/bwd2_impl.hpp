@@ -299,11 +299,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // K and V fragments (MFMA B operand) of this lane's key row, and those of
-  // the next unit with steps (kn, vn), loaded one unit ahead.  Loads the
-  // compiler sees: it waits for them before any use or register copy (an
-  // asm load's outputs would count as ready at once).
-  bf16x8 kf[NKK], vf[NKK], kn[NKK], vn[NKK];
+  // K and V fragments (MFMA B operand) of this lane's key row.  The next unit
+  // with steps loads into them right after their last use (the S/dP MFMAs of
+  // the unit's last step), before that step's P/dS work and the unit's
+  // stores: the wait at their first use then covers neither.  Loads the
+  // compiler sees: it waits for them before any use (an asm load's outputs
+  // would count as ready at once).
+  bf16x8 kf[NKK], vf[NKK];
   auto load_kv = [&](const Unit& x) __attribute__((always_inline)) {
     const int64_t ko = ((int64_t)x.s.k0 * H + x.h) * D;
     const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(A_k) + ko, (uint32_t)x.s.lk * HD * 2);
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint32_t voff = (uint32_t)(key * HD + kk * 16 + g * 8) * 2;
-      kn[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, voff));
-      vn[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, voff));
+      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, voff));
+      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, voff));
     }
   };
 
@@ -649,19 +651,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       dvacc[d] = f32x16{};
     }
     if (x.n > 0) {
-      // this unit's K/V (loaded one unit ahead); then the next unit's
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        kf[kk] = kn[kk];
-        vf[kk] = vn[kk];
-      }
-      for (int un = u + 1; un < u_end; ++un) {
-        const Unit xn = fetch(un);
-        if (xn.n > 0) {
-          load_kv(xn);
-          break;
-        }
-      }
       // prologue: S/dP of step 0
       acquire();
       produce();
@@ -679,6 +668,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         dkdv_mma(cs, ops, dkacc, dvacc);
         cur = nxt;
         cs = cn;
+      }
+      // K/V are free: the next unit with steps loads its own
+      for (int un = u + 1; un < u_end; ++un) {
+        const Unit xn = fetch(un);
+        if (xn.n > 0) {
+          load_kv(xn);
+          break;
+        }
       }
       dkdv_mma(cs, softmax(x, x.n - 1, cs, cur), dkacc, dvacc);
     }
