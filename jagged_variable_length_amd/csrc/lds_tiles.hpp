@@ -40,17 +40,19 @@ __device__ __forceinline__ i32x4 rsrc_at(const i32x4& r, int64_t bytes_off, int6
 // the 2-byte value zero-extended).  Issued as inline asm so that the compiler
 // does not attach its own conservative vmcnt waits to unrelated LDS reads; the
 // kernels wait for these loads explicitly (s_waitcnt vmcnt + barrier) before
-// reading the data.
+// reading the data.  A write of M0 followed by an LDS-DMA load needs one wait
+// state on this target (the compiler puts an s_nop between them for its own
+// LDS-DMA loads; inline asm gets no hazard padding, so it is written here).
 __device__ __forceinline__ void lds_dma16(const i32x4& r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const i32x4& r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
 __device__ __forceinline__ void lds_dma2(const i32x4& r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
                : "memory");
 }
 
