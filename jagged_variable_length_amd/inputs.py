@@ -51,6 +51,7 @@ class Workload:
     qk_norm: bool = False  # Q and K rows L2-normalised before attention (and in the backward)
     scale: Optional[float] = None  # score scale; None = 1/sqrt(D)
     rope: bool = False  # block mode: rotary embedding of Q and K fused into the kernels
+    seed: Optional[int] = None  # canonical seed; None = the workload index
 
 
 WORKLOADS = {
@@ -69,6 +70,10 @@ WORKLOADS = {
     # BlockAttention (workload 4's shapes) with the rotary embedding fused in
     7: Workload("block_attention_64_rope", 64, 4, 128, "bf16", ACT_SOFTMAX, True, False, False, "bf16", "bf16",
                 False, rope=True),
+    # workload 1 without the bias (and dBias): the forward is no longer
+    # bound by the bias stream
+    8: Workload("jfa_self_nobias", 256, 4, 128, "bf16", ACT_SOFTMAX, False, False, False, "bf16", "bf16", False,
+                seed=1),
 }
 
 
@@ -114,7 +119,7 @@ def _lengths_from(rng, cfg):
         lq = rng.integers(1, 65, w.B).astype(np.int64)
         lq[1] = 0  # one zero-length sample
         return lq, lq.copy()
-    if cfg == 1:
+    if cfg in (1, 8):
         lq = _lognormal_lengths(rng, w.B, 300, 8, 1000)
         return lq, lq.copy()
     if cfg == 2:
@@ -199,7 +204,8 @@ def generate(lq, lk, H, D, dtype, *, rng, bias=False, bias_std=0.1, dout=True) -
 def make_inputs(cfg: int, seed: Optional[int] = None, dout: bool = True) -> JaggedInputs:
     """Inputs of workload ``cfg``; the canonical seed is the config index."""
     w = WORKLOADS[cfg]
-    seed = cfg if seed is None else seed
+    if seed is None:
+        seed = cfg if w.seed is None else w.seed
     rng = np.random.default_rng(seed)
     lq, lk = _lengths_from(rng, cfg)
     return generate(lq, lk, w.H, w.D, w.dtype, rng=rng, bias=w.bias, dout=dout)

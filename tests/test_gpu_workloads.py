@@ -16,7 +16,7 @@ from gpu_util import TOL, check, say  # noqa: E402
 
 def _setup(cfg):
     w = gen.WORKLOADS[cfg]
-    inp = gen.make_inputs(cfg, cfg)
+    inp = gen.make_inputs(cfg)  # canonical seed of the workload
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
                            has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands,
@@ -39,7 +39,7 @@ def _pick_samples(inp, rng):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 8])
 def test_dense_workload_full_size(cfg):
     say(f"case: workload {cfg} full size")
     w, inp, op, d = _setup(cfg)
