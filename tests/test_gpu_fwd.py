@@ -8,7 +8,7 @@ from jagged_variable_length_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, check_lse, device_inputs, make_op, oracle_fwd, say, sync  # noqa: E402
+from gpu_util import check, check_lse, device_inputs, make_op, oracle_bwd, oracle_fwd, say, sync  # noqa: E402
 from oracle import attention as ora  # noqa: E402
 
 
@@ -127,3 +127,34 @@ def test_fwd_orders_agree(order):
     o2, l2 = op2.forward(d["q"], d["k"], d["v"])
     sync()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("lq", [[5, 40, 70], [300, 260, 1]])
+def test_fwd_bwd_adversarial_negative_bias(lq):
+    """Subtraction scheme near its documented limit: every valid score sits
+    around -5.5 (bias -5.5, Q K^T nearly zero) while the zero-filled tail
+    keys score 0, so the row sum is n_pad + sum(e^s) - n_pad in fp32.  With at
+    most 127 padded keys the cancellation leaves a relative error of about
+    ulp(128) / e^-5.5 ~ 2e-3 in P, which dBias (up to ~10 here) carries
+    inside the bound; far below that it would not (the limit is stated with
+    the scheme's readings).  P and dS enter the
+    dV / dK products as hi + lo pairs: with 260 queries on 2 keys, bf16 P
+    alone would move dV by ~0.05 (the long-query, few-key shape of the
+    cross-attention workload, which runs with split operands too)."""
+    say(f"case: adversarial negative bias lq={lq}")
+    lk = [1, 2, 31]
+    inp = gen.make_custom(lq, lk, 2, 64, "bf16", seed=13, bias=True)
+    rng = np.random.default_rng(13)
+    inp.q = gen.f32_to_bf16_bits(0.01 * rng.standard_normal(inp.q.shape).astype(np.float32))
+    inp.bias = gen.f32_to_bf16_bits((-5.5 + 0.1 * rng.standard_normal(inp.bias.shape)).astype(np.float32))
+    op = make_op(inp, bias=True, want_dbias=True, out_dtype="f32", grad_dtype="f32", split=True)
+    d = device_inputs(inp)
+    o, lse = op.forward(d["q"], d["k"], d["v"], bias=d["bias"])
+    dq, dk, dv, db = op.backward(d["q"], d["k"], d["v"], d["dout"], o=o, lse=lse, bias=d["bias"])
+    sync()
+    ro, rl = oracle_fwd(inp, op)
+    check(A.to_f64(o), ro, "O")
+    check_lse(A.to_f64(lse), rl)
+    rg = oracle_bwd(inp, op)
+    for name, g, r in zip(["dQ", "dK", "dV", "dBias"], (dq, dk, dv, db), rg):
+        check(A.to_f64(g), r, name)
