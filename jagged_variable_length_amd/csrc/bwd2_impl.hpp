@@ -38,6 +38,8 @@
 // window, branch-free inside the interleaved loop.  dBias is not produced
 // with a window (its dense [lq, lk] layout would be mostly zeros).
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
@@ -390,6 +392,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   struct Ops {
     bf16x8 ph[2], dh[2], pl[2], dl[2];
   };
+  // whether this wave's 32x32 block of step t lies wholly inside the window
+  // (its queries and keys inside the sample): then it needs no mask
+  auto block_full = [&](const Unit& x, int t) __attribute__((always_inline)) {
+    const Window w{A_win_l, A_win_r, x.s.lq, x.s.lk};
+    return w.full(step_row0(x, t) + wq * 32, x.kt * KT + wv * 32);
+  };
   auto softmax = [&](const Unit& x, int t, int st, const SD& sd) __attribute__((always_inline)) {
     const f32x16 sacc = sd.s, dpacc = sd.dp;
     Ops o;
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         ds[i] = act_grad(ACT, xv) * dpacc[i];
       }
     }
-    if constexpr (WIN) {
+    if (WIN && !block_full(x, t)) {
       const int key = x.kt * KT + wv * 32 + l32;
       const int rbase = step_row0(x, t) + wq * 32 + g * 4;
 #pragma unroll
@@ -500,8 +508,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // P/dS (and its dBias store) of step t in stage cs; a scheduling fence
   // after each pair keeps that order, so the matrix core and the VALU work
   // side by side.  Operand LDS reads run two MFMAs ahead.
-  auto sdp_softmax = [&](int cn, const Unit& x, int t, int cs_, const SD& cur, SD& nx,
+  // MASK (windowed kernels): apply the window mask to P and dS; instances
+  // with and without it keep the interleaved loop free of branches
+  auto sdp_softmax = [&](auto mask_tag, int cn, const Unit& x, int t, int cs_, const SD& cur, SD& nx,
                          Ops& o) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* qn = smem + cn * Sh::STAGE;
     const char* on = qn + Sh::OFF_O;
     const char* qt = smem + cs_ * Sh::STAGE;
@@ -572,7 +583,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         p[c] = act_fwd(ACT, xv);
         ds[c] = act_grad(ACT, xv) * dpv;
       }
-      if constexpr (WIN) {
+      if constexpr (MASK) {
         const bool ok = window_ok(x, wkey - wrbase, wrbase, wkey, c);
         p[c] = ok ? p[c] : 0.0f;
         ds[c] = ok ? ds[c] : 0.0f;
@@ -664,7 +675,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         patch_tail(x, t + 1, cn);
         SD nxt;
         Ops ops;
-        sdp_softmax(cn, x, t, cs, cur, nxt, ops);
+        if (WIN && !block_full(x, t))
+          sdp_softmax(std::true_type{}, cn, x, t, cs, cur, nxt, ops);
+        else
+          sdp_softmax(std::false_type{}, cn, x, t, cs, cur, nxt, ops);
         dkdv_mma(cs, ops, dkacc, dvacc);
         cur = nxt;
         cs = cn;
