@@ -28,7 +28,23 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 class JaggedAttention:
-    """One jagged batch layout (offsets + options) bound to a plan."""
+    """One jagged batch layout (offsets + options) bound to a plan.
+
+    Values are [T, H, D] tensors with samples concatenated along T; the
+    offsets are host int64 arrays [B + 1].  Options map one to one onto the
+    C descriptor (include/jattn.h):
+      act            "softmax", "gelu" (erf GELU), "silu", or "gelu_poly" (the
+                     ALU-only polynomial GELU, meant for QK-normed inputs)
+      block_diagonal fixed 64-token blocks (BlockAttention); with rope=True the
+                     rotary embedding of Q and K is fused into the block kernels
+                     (rope_base <= 0 selects 10000)
+      window         (left, right): sliding window, query i sees keys
+                     i - left .. i + right of its own sample (lq == lk)
+      has_bias / want_dbias, dtypes, split_operands (hi + lo bf16 operands for
+                     the P / dS products), order and num_workers of the plan.
+    forward() returns (O, LSE); backward() returns (dQ, dK, dV, dBias).  QK-norm
+    itself is qk_norm() / qk_norm_backward() below.
+    """
 
     def __init__(self, q_offsets, kv_offsets, H: int, D: int, *, act: str = "softmax",
                  block_diagonal: bool = False, has_bias: bool = False, want_dbias: bool = False,
