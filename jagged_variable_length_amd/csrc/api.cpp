@@ -450,7 +450,7 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
     a.H = p->H;
     a.scale = p->scale;
     a.scale_log2 = p->scale * 1.4426950408889634f;
-    e = jattn::launch_block_bwd(a, sel, p->block.num_workers / 2, st);
+    e = jattn::launch_block_bwd(a, sel, p->block.num_workers, st);  // one wave pair per workgroup
     if (e != hipSuccess) return hip_fail(e, "block backward launch");
     return ok();
   }

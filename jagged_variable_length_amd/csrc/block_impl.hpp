@@ -12,7 +12,8 @@
 //           64-key softmax row lives in one lane, so one pass computes m, l
 //           and P; the zero rows of a partial last block are removed by
 //           subtracting their exp(0 - m) terms.
-// Backward: two waves per block (two blocks per workgroup).  Phase 1, lane =
+// Backward: two waves per block, one block per workgroup (two workgroups
+//           share a CU and run independently).  Phase 1, lane =
 //           query row: S^T, softmax, dP^T, Di = sum_j P dP (in-tile), dS,
 //           dQ = dS K.  Phase 2, lane = key row: S, dP again, P from the
 //           phase-1 row statistics, dV = P^T dO, dK = dS^T Q.
@@ -87,7 +88,7 @@ __device__ __forceinline__ double rope_theta(const double* t, int j) { return t[
 // copy the D/2 angles of the plan's table into LDS (before a barrier)
 template <int D>
 __device__ __forceinline__ void stage_theta(double* dst, const double* src) {
-  for (int j = threadIdx.x; j < D / 2; j += kThreads) dst[j] = src[j];
+  for (int j = threadIdx.x; j < D / 2; j += blockDim.x) dst[j] = src[j];
 }
 
 // cos and sin of m * theta: the angle is formed and reduced to [-pi, pi] in
@@ -336,48 +337,46 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: a wave pair per block, two pairs per workgroup in lockstep
+// backward: one wave pair per workgroup and per block
 // ---------------------------------------------------------------------------
+// A workgroup is one wave pair with its own worker list, so its barriers
+// involve only the pair: two such workgroups fit in one CU's LDS and drift
+// apart, and one pair's tile loads overlap the other's MFMA and softmax work.
+constexpr int kPairThreads = 128;
+
 template <typename TG, int D, bool ROPE = false>
-__global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kPairThreads, 1) void block_bwd_kernel(BwdArgs a) {
   using T = Tile<D>;
   constexpr int NKK = D / 16, ND = D / 32;
   constexpr int PAIR_BYTES = 4 * T::BYTES + 2 * 64 * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * PAIR_BYTES];
+  static_assert(2 * (PAIR_BYTES + (ROPE ? D * 4 : 8)) <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) char smem[PAIR_BYTES];
   __shared__ double theta_s[ROPE ? D / 2 : 1];
   if constexpr (ROPE) {
     stage_theta<D>(theta_s, a.rope_theta);
     __syncthreads();
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w2 = threadIdx.x >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int pair = wave >> 1, w2 = wave & 1;
-  char* qt = smem + pair * PAIR_BYTES;
+  char* qt = smem;
   char* kt = qt + T::BYTES;
   char* vt = kt + T::BYTES;
   char* ot = vt + T::BYTES;  // dO
   float* L2s = reinterpret_cast<float*>(ot + T::BYTES);
   float* Dis = L2s + 64;
-  // each wave pair walks its own worker list; the two pairs of a workgroup
-  // run the same number of rounds so that every barrier is reached by all
-  const int wbase = xcd_worker(blockIdx.x, gridDim.x) * 2;
-  const int u0 = a.worker_off[wbase + pair], u1 = a.worker_off[wbase + pair + 1];
-  const int rounds = max(a.worker_off[wbase + 1] - a.worker_off[wbase], a.worker_off[wbase + 2] - a.worker_off[wbase + 1]);
+  const int worker = xcd_worker(blockIdx.x, gridDim.x);
+  const int u_end = a.worker_off[worker + 1];
   const int HD = a.H * D;
 
-  for (int k = 0; k < rounds; ++k) {
-    const int u = u0 + k;
-    const bool active = u < u1;
-    int r = 0, row0 = 0;
-    int64_t qbase = 0, kbase = 0;
-    if (active) {
-      const i32x4 unit = load_unit(a.units, u);
-      const int b = unit[0], h = unit[1], t = unit[2];
-      const Sample s = load_sample(a.samples, b);
-      row0 = t * 64;
-      r = min(64, s.lq - row0);
-      qbase = ((int64_t)(s.q0 + row0) * a.H + h) * D;
-      kbase = ((int64_t)(s.k0 + row0) * a.H + h) * D;
+  for (int u = a.worker_off[worker]; u < u_end; ++u) {
+    const i32x4 unit = load_unit(a.units, u);
+    const int b = unit[0], h = unit[1], t = unit[2];
+    const Sample s = load_sample(a.samples, b);
+    const int row0 = t * 64;
+    const int r = min(64, s.lq - row0);
+    const int64_t qbase = ((int64_t)(s.q0 + row0) * a.H + h) * D;
+    const int64_t kbase = ((int64_t)(s.k0 + row0) * a.H + h) * D;
+    {
       const uint32_t nbytes = (uint32_t)r * HD * 2;
       const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qbase, nbytes);
       const rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kbase, nbytes);
@@ -393,22 +392,19 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
     // rotate its share of the Q and K tiles once, then the dQ and dK rows in
     // the epilogues
     float rc[ROPE ? D / 4 : 1], rs[ROPE ? D / 4 : 1];
-    if constexpr (ROPE)
-      if (active) rope_lane_angles<D>(theta_s, row0 + w2 * 32 + l32, g, rc, rs);
+    if constexpr (ROPE) rope_lane_angles<D>(theta_s, row0 + w2 * 32 + l32, g, rc, rs);
     wait_vmem();
     __syncthreads();
     if constexpr (ROPE) {
-      if (active) {
-        rope_lane_lds<D>(qt, w2 * 32 + l32, g, rc, rs);
-        rope_lane_lds<D>(kt, w2 * 32 + l32, g, rc, rs);
-      }
+      rope_lane_lds<D>(qt, w2 * 32 + l32, g, rc, rs);
+      rope_lane_lds<D>(kt, w2 * 32 + l32, g, rc, rs);
       wait_lds();
       __syncthreads();
     }
 
     const int npad = 64 - r;
     // ---- phase 1: lane = query row (w2*32 + l32) ----
-    if (active) {
+    {
       bf16x8 qf[NKK], of[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -491,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_bwd_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---- phase 2: lane = key row (w2*32 + l32) ----
-    if (active) {
+    {
       bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {

@@ -16,9 +16,9 @@ hipError_t fwd_r(const FwdArgs& a, bool out_f32, int grid, hipStream_t st) {
 template <int D, bool ROPE>
 hipError_t bwd_r(const BwdArgs& a, bool grad_f32, int grid, hipStream_t st) {
   if (grad_f32)
-    hipLaunchKernelGGL((block_bwd_kernel<float, D, ROPE>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((block_bwd_kernel<float, D, ROPE>), dim3(grid), dim3(kPairThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((block_bwd_kernel<bf16, D, ROPE>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((block_bwd_kernel<bf16, D, ROPE>), dim3(grid), dim3(kPairThreads), 0, st, a);
   return hipGetLastError();
 }
 template <int D>
