@@ -295,7 +295,7 @@ def _cpu_baseline_rope(w, inp, q, k, v, do, scale, budget_s, cores):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs (--gpus > 1) are not supported "
+        print("bench.py: measures one GPU only; multi-GPU runs (--gpus > 1) are not supported "
               "(attention has no cross-GPU exchange; the sharding design is per-sample data parallel)",
               file=sys.stderr)
         sys.exit(2)
