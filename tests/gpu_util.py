@@ -64,6 +64,18 @@ def check(got, ref, name, tol=TOL):
     return err
 
 
+def check_dbias(got, ref, name="dBias", tol=TOL):
+    """dBias against the 2e-2 bound and also against its own scale: dBias
+    elements shrink with the number of keys (about 1e-3 on long samples), so
+    the absolute bound alone would not see a value written to the wrong
+    place; a misplaced value errs by the order of max|ref|, a correct one by
+    well under 1 % of it here."""
+    err = check(got, ref, name, tol)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    assert err <= 0.1 * scale + 1e-4, f"{name}: max abs error {err} against max|ref| {scale}"
+    return err
+
+
 def check_lse(got, ref, tol=TOL):
     fin = np.isfinite(ref)
     assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "LSE -inf pattern differs"

@@ -57,6 +57,7 @@ def _desc(**kw):
     d.num_workers = kw.get("num_workers", 0)
     d.window_left, d.window_right = kw.get("window", (0, 0))
     d.rope, d.rope_base = kw.get("rope", 0), kw.get("rope_base", 0.0)
+    d.dbias_dtype = kw.get("dbias_dtype", B.JATTN_BF16)
     return d
 
 
@@ -99,6 +100,32 @@ def test_plan_create_rejects(lib, kw, qo, ko, code):
         B.jattn_plan_create(d, qo, ko)
     assert e.value.code == code
     assert B.jattn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,L,ok", [
+    # one sample's rows must span < 2^31 bytes (H * D * 2 = 512 bytes a row)
+    (dict(B=1, H=2, D=128), (1 << 22) - 1, True),
+    (dict(B=1, H=2, D=128), 1 << 22, False),
+    # a head's bf16 bias block must span < 2^30 bytes: 23170^2 * 2 < 2^30 <= 23171^2 * 2
+    (dict(B=1, has_bias=1), 23170, True),
+    (dict(B=1, has_bias=1), 23171, False),
+    # a head's fp32 dBias block must span < 2^30 bytes: 16383^2 * 4 < 2^30 = 16384^2 * 4
+    (dict(B=1, has_bias=1, want_dbias=1, dbias_dtype=B.JATTN_F32), 16383, True),
+    (dict(B=1, has_bias=1, want_dbias=1, dbias_dtype=B.JATTN_F32), 16384, False),
+    (dict(B=1, has_bias=1, want_dbias=1), 23170, True),
+])
+def test_per_sample_size_limits(lib, kw, L, ok):
+    """The largest per-sample sizes are accepted, one more row is refused
+    (every per-(sample, head) byte offset stays inside the 32-bit range of a
+    buffer descriptor); plan creation is host-only."""
+    d = _desc(**kw)
+    if ok:
+        p = B.jattn_plan_create(d, [0, L], [0, L])
+        B.jattn_plan_destroy(p)
+    else:
+        with pytest.raises(B.JattnError) as e:
+            B.jattn_plan_create(d, [0, L], [0, L])
+        assert e.value.code == B.JATTN_E_SHAPE
 
 
 def test_null_arguments(lib):

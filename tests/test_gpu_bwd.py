@@ -8,7 +8,7 @@ from jagged_variable_length_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, device_inputs, make_op, oracle_bwd, say, sync  # noqa: E402
+from gpu_util import check, check_dbias, device_inputs, make_op, oracle_bwd, say, sync  # noqa: E402
 
 
 def _run(inp, **kw):
@@ -26,7 +26,7 @@ def _compare(inp, op, got):
     for name, g, r in zip(["dQ", "dK", "dV", "dBias"], got, ref):
         if r is None:
             continue
-        check(g, r, name)
+        (check_dbias if name == "dBias" else check)(g, r, name)
 
 
 def test_bwd_config0_f32():

@@ -11,7 +11,7 @@ from oracle import attention as ora
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-from gpu_util import TOL, check, say  # noqa: E402
+from gpu_util import TOL, check, check_dbias, say  # noqa: E402
 
 
 def _setup(cfg):
@@ -67,7 +67,7 @@ def test_dense_workload_full_size(cfg):
         check(dk[sk], rg[1], "dK")
         check(dv[sk], rg[2], "dV")
         if w.want_dbias:
-            check(db[bst[b]:bst[b + 1]], rg[3], "dBias")
+            check_dbias(db[bst[b]:bst[b + 1]], rg[3])
 
 
 def test_block_workload_full_size():
