@@ -27,6 +27,25 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _args(*specs):
+    """Pointers of the tensors the library reads or writes, each spec being
+    (tensor or None, name, dtype, elements the call touches).  The C ABI takes
+    bare pointers, so a tensor of the wrong type or with too few elements is
+    refused here (a kernel would read or write past its end): types and sizes
+    of all tensors first, then that each is a contiguous device tensor."""
+    for t, name, dtype, numel in specs:
+        if t is None:
+            continue
+        if t.dtype != _TORCH_DT[dtype]:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {_TORCH_DT[dtype]}")
+        if t.numel() < numel:
+            raise ValueError(f"{name}: {t.numel()} elements, the plan needs {numel}")
+    for t, name, _, _ in specs:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name}: must be a device tensor")
+    return [_ptr(t) for t, _, _, _ in specs]
+
+
 class JaggedAttention:
     """One jagged batch layout (offsets + options) bound to a plan.
 
@@ -99,19 +118,33 @@ class JaggedAttention:
     def _stream(self):
         return torch.cuda.current_stream(self.device).cuda_stream
 
+    def _inputs(self, q, k, v, bias):
+        nq, nk = self.Tq * self.H * self.D, self.Tk * self.H * self.D
+        nb = int(self.info.bias_elems) if self.has_bias else 0
+        return [(q, "q", self.in_dtype, nq), (k, "k", self.in_dtype, nk), (v, "v", self.in_dtype, nk),
+                (bias, "bias", self.in_dtype, nb)]
+
     def forward(self, q, k, v, bias=None, o=None, lse=None, want_lse=True):
+        pq, pk, pv, pb, _, _ = _args(*self._inputs(q, k, v, bias), (o, "o", self.out_dtype, self.Tq * self.H * self.D),
+                                     (lse, "lse", "f32", self.Tq * self.H))
         if self.workspace is None:
             self.upload()
         if o is None:
             o = torch.empty(self.Tq, self.H, self.D, dtype=_TORCH_DT[self.out_dtype], device=self.device)
         if lse is None and want_lse and self.act == "softmax" and not self.block_diagonal:
             lse = torch.empty(self.Tq, self.H, dtype=torch.float32, device=self.device)
-        _b.jattn_fwd(self.plan, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse),
-                     self.workspace.data_ptr(), self._stream())
+        _b.jattn_fwd(self.plan, pq, pk, pv, pb, _ptr(o), _ptr(lse), self.workspace.data_ptr(), self._stream())
         return o, lse
 
     def backward(self, q, k, v, dout, o=None, lse=None, bias=None, dq=None, dk=None, dv=None, dbias=None,
                  stages=_b.JATTN_BWD_ALL):
+        nq, nk = self.Tq * self.H * self.D, self.Tk * self.H * self.D
+        pq, pk, pv, pb = _args(*self._inputs(q, k, v, bias), (o, "o", self.out_dtype, nq),
+                               (lse, "lse", "f32", self.Tq * self.H), (dout, "dout", self.in_dtype, nq),
+                               (dq, "dq", self.grad_dtype, nq), (dk, "dk", self.grad_dtype, nk),
+                               (dv, "dv", self.grad_dtype, nk),
+                               (dbias, "dbias", self.dbias_dtype,
+                                int(self.info.bias_elems) if self.want_dbias else 0))[:4]
         if self.workspace is None:
             self.upload()
         gdt = _TORCH_DT[self.grad_dtype]
@@ -120,7 +153,7 @@ class JaggedAttention:
         dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
         if self.want_dbias and dbias is None:
             dbias = torch.empty(int(self.info.bias_elems), dtype=_TORCH_DT[self.dbias_dtype], device=self.device)
-        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+        args = (pq, pk, pv, pb, _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                 _ptr(dv), _ptr(dbias), self.workspace.data_ptr(), self._stream())
         if stages == _b.JATTN_BWD_ALL:
             _b.jattn_bwd(self.plan, *args)
@@ -144,10 +177,12 @@ def qk_norm(x: torch.Tensor, out_dtype: Optional[str] = None, out: Optional[torc
     by the library's kernel.  Returns (y, rnorm) with rnorm = 1 / max(||x||, eps)."""
     D = x.shape[-1]
     rows = x.numel() // D
-    odt = out_dtype or _DT_OF[x.dtype]
+    xdt = _DT_OF[x.dtype]
+    odt = out_dtype or (_DT_OF[out.dtype] if out is not None else xdt)
+    px = _args((x, "x", xdt, x.numel()), (out, "out", odt, x.numel()), (rnorm, "rnorm", "f32", rows))[0]
     y = out if out is not None else torch.empty(x.shape, dtype=_TORCH_DT[odt], device=x.device)
     r = rnorm if rnorm is not None else torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _b.jattn_l2norm_fwd(_ptr(x), _ptr(y), _ptr(r), rows, D, _DT[_DT_OF[x.dtype]], _DT[odt],
+    _b.jattn_l2norm_fwd(px, _ptr(y), _ptr(r), rows, D, _DT[xdt], _DT[odt],
                         torch.cuda.current_stream(x.device).cuda_stream)
     return y, r
 
@@ -157,9 +192,11 @@ def qk_norm_backward(x: torch.Tensor, dy: torch.Tensor, out_dtype: Optional[str]
     """QK-norm backward: dL/dx from the forward input x and dL/dy."""
     D = x.shape[-1]
     rows = x.numel() // D
-    odt = out_dtype or _DT_OF[dy.dtype]
+    xdt, gdt = _DT_OF[x.dtype], _DT_OF[dy.dtype]
+    odt = out_dtype or (_DT_OF[out.dtype] if out is not None else gdt)
+    px, pdy, _ = _args((x, "x", xdt, x.numel()), (dy, "dy", gdt, x.numel()), (out, "out", odt, x.numel()))
     dx = out if out is not None else torch.empty(x.shape, dtype=_TORCH_DT[odt], device=x.device)
-    _b.jattn_l2norm_bwd(_ptr(x), _ptr(dy), _ptr(dx), rows, D, _DT[_DT_OF[x.dtype]], _DT[_DT_OF[dy.dtype]],
+    _b.jattn_l2norm_bwd(px, pdy, _ptr(dx), rows, D, _DT[xdt], _DT[gdt],
                         _DT[odt], torch.cuda.current_stream(x.device).cuda_stream)
     return dx
 
