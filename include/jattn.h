@@ -106,7 +106,7 @@ typedef struct jattn_plan jattn_plan; /* opaque */
 typedef struct {
   int32_t B, H, D;      /* D in {32, 64, 128}; H >= 1; B >= 0 */
   float scale;          /* softmax/GDPA scale; <= 0 selects 1/sqrt(D) */
-  int32_t act;          /* JATTN_SOFTMAX | JATTN_GELU_ERF | JATTN_SILU */
+  int32_t act;          /* JATTN_SOFTMAX | JATTN_GELU_ERF | JATTN_SILU | JATTN_GELU_POLY */
   int32_t mask;         /* JATTN_MASK_NONE | JATTN_MASK_BLOCKDIAG64 | JATTN_MASK_WINDOW */
   int32_t has_bias;     /* 0/1: additive bias input */
   int32_t want_dbias;   /* 0/1: backward writes dBias (needs has_bias) */
