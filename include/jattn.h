@@ -39,10 +39,19 @@
  * Ownership and threading.  The caller owns every device buffer, including
  * the workspace (size from jattn_plan_info).  The library never allocates
  * device memory.  A plan is host memory owned by the library, immutable
- * after creation and safe to share between threads.  Work is enqueued on
- * the given stream (a hipStream_t; NULL = the null stream) and the call
- * returns without waiting; device faults surface at the caller's next
- * synchronisation.  Two calls in flight must not share one workspace.
+ * after creation and safe to share between threads.  jattn_fwd, jattn_bwd
+ * and jattn_bwd_stages enqueue their kernels on the given stream (a
+ * hipStream_t; NULL = the null stream) and return without waiting; device
+ * faults surface at the caller's next synchronisation.  jattn_plan_upload is
+ * the exception: it waits for its copy (see there).
+ *
+ * Sharing one workspace.  The workspace holds the uploaded plan, which every
+ * call only reads, and a scratch region (row statistics Di and LSE * log2 e)
+ * that the backward's PREP stage writes and its DKDV and DQ stages read.
+ * Forwards may therefore run concurrently on one workspace; DKDV and DQ may
+ * run concurrently with each other (jattn_bwd_stages) once PREP is done; a
+ * call that runs PREP (every jattn_bwd of a softmax plan without the block
+ * mask) must not overlap another backward on the same workspace.
  *
  * Errors.  Every call returns JATTN_OK (0) or a negative JATTN_E_* code.
  * Arguments are validated on the host before anything is enqueued; on
@@ -114,7 +123,15 @@ typedef struct {
   int32_t out_dtype;    /* o */
   int32_t grad_dtype;   /* dq, dk, dv */
   int32_t split_operands; /* 0/1: P and dS enter the PV-type products as
-                             bf16 hi + lo pairs (two MFMAs) for accuracy */
+                             bf16 hi + lo pairs (two MFMAs) for accuracy.
+                             Accuracy contract: GDPA (GELU / SiLU) rows are
+                             not normalised, so with plain bf16 P the error of
+                             O = P V grows as 2^-8 sum_j |P_ij| |V_j| (about
+                             0.15 at 4000 keys of N(0,1) data); a 2e-2
+                             max-abs bound on long key sets needs split = 1
+                             and fp32 outputs.  Softmax normalises by the sum
+                             of the rounded P and does not need it; for dV /
+                             dK sums over thousands of queries it does. */
   int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
   int32_t num_workers;  /* persistent workers per kernel; 0 = default */
   int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
@@ -170,13 +187,22 @@ int jattn_plan_info(const jattn_plan* plan, jattn_plan_summary* summary);
 int jattn_plan_export(const jattn_plan* plan, int32_t which, int32_t* dst, int64_t cap,
                       int64_t* n);
 
-/* Enqueue a copy of the plan into the caller's device workspace.  Must be
- * done once per (plan, workspace) pair before jattn_fwd / jattn_bwd use that
- * workspace; the plan region is never modified by fwd/bwd. */
+/* Copy the plan into the caller's device workspace, on `stream`, and wait
+ * for the copy to finish (hipStreamSynchronize(stream)): the call blocks the
+ * host until everything enqueued on that stream before it has run, and the
+ * plan's host memory may then be freed.  Must be done once per (plan,
+ * workspace) pair before jattn_fwd / jattn_bwd use that workspace; the plan
+ * region is never modified by fwd/bwd. */
 int jattn_plan_upload(const jattn_plan* plan, void* workspace, int64_t workspace_bytes,
                       void* stream);
 
 /* Forward.  Writes o (out_dtype) and, for softmax with mask NONE or WINDOW, lse.
+ * Tail handling ("Jagged Sequence Flash Attention" section): keys past a
+ * sample's end are read as zeros and score 0; their exp terms are removed
+ * from the row sum by subtraction instead of a -inf mask.  A row whose best
+ * valid score is below 0 (where the subtraction would cancel or, once the
+ * valid terms underflow, give NaN) instead drops those keys in the one key
+ * step that holds them, so any finite bias is handled exactly.
  * bias: required iff desc.has_bias.  lse may be NULL (not written) for
  * softmax; it must be NULL-or-ignored for GDPA and block mode, which keep
  * no row statistics ("BlockAttention" section: no logsumexp traffic). */

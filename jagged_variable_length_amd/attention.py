@@ -59,8 +59,11 @@ class JaggedAttention:
                      (rope_base <= 0 selects 10000)
       window         (left, right): sliding window, query i sees keys
                      i - left .. i + right of its own sample (lq == lk)
-      has_bias / want_dbias, dtypes, split_operands (hi + lo bf16 operands for
-                     the P / dS products), order and num_workers of the plan.
+      has_bias / want_dbias, dtypes, order and num_workers of the plan.
+      split_operands hi + lo bf16 operands for the P / dS products.  Default
+                     (None): on for the GDPA activations, whose unnormalised
+                     P V over long key sets errs by up to 2^-8 sum|P||V| with
+                     plain bf16 P (about 0.15 at 4000 keys), off for softmax.
     forward() returns (O, LSE); backward() returns (dQ, dK, dV, dBias).  QK-norm
     itself is qk_norm() / qk_norm_backward() below.
     """
@@ -68,7 +71,7 @@ class JaggedAttention:
     def __init__(self, q_offsets, kv_offsets, H: int, D: int, *, act: str = "softmax",
                  block_diagonal: bool = False, has_bias: bool = False, want_dbias: bool = False,
                  in_dtype: str = "bf16", out_dtype: Optional[str] = None,
-                 grad_dtype: Optional[str] = None, split_operands: bool = False,
+                 grad_dtype: Optional[str] = None, split_operands: Optional[bool] = None,
                  order: str = "zigzag", num_workers: int = 0, scale: Optional[float] = None,
                  dbias_dtype: Optional[str] = None, window: Optional[tuple] = None, rope: bool = False,
                  rope_base: float = 0.0, device="cuda"):
@@ -97,6 +100,9 @@ class JaggedAttention:
         d.rope, d.rope_base = int(rope), float(rope_base)
         d.has_bias, d.want_dbias = int(has_bias), int(want_dbias)
         d.in_dtype, d.out_dtype, d.grad_dtype = _DT[in_dtype], _DT[self.out_dtype], _DT[self.grad_dtype]
+        if split_operands is None:
+            split_operands = act != "softmax"
+        self.split_operands = bool(split_operands)
         d.split_operands = int(split_operands)
         d.order = _ORDER[order]
         d.num_workers = num_workers
@@ -116,7 +122,13 @@ class JaggedAttention:
         return self
 
     def _stream(self):
-        return torch.cuda.current_stream(self.device).cuda_stream
+        """The current stream, on which the call is enqueued.  The workspace
+        was allocated on the stream current at upload(); recording this one
+        keeps the caching allocator from handing its memory out again while
+        work enqueued here may still read it."""
+        cur = torch.cuda.current_stream(self.device)
+        self.workspace.record_stream(cur)
+        return cur.cuda_stream
 
     def _inputs(self, q, k, v, bias):
         nq, nk = self.Tq * self.H * self.D, self.Tk * self.H * self.D

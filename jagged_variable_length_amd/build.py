@@ -27,25 +27,28 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
-# (source, object name, extra defines)
-# (D, input type, output/gradient type) instances of the fp32 forward and the backward
-FWD_INST = [(128, "bf16", "bf16"), (128, "bf16", "f32"), (64, "bf16", "bf16"), (64, "bf16", "f32"),
-            (64, "f32", "f32"), (32, "bf16", "bf16"), (32, "bf16", "f32"), (32, "f32", "f32")]
+# fp32 inputs (with fp32 outputs and gradients) run the first-generation
+# forward and backward kernels (fwd_inst.hip, bwd_inst.hip); bf16 inputs run
+# the LDS-DMA kernels (fwd2/dkdv2/dq2) and take only the Di pass from
+# bwd_inst.hip.
+F32_DIMS = (64, 32)
+BF16_DIMS = (128, 64, 32)
 
 
 def units():
+    """(source, object name, extra defines) of every translation unit."""
     u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", []),
          ("l2norm.hip", "l2norm", [])]
-    for d in (128, 64, 32):
+    for d in BF16_DIMS:
         u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
         for tg in ("bf16", "f32"):
             u.append(("bwd2_inst.hip", f"dkdv2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
             u.append(("dq2_inst.hip", f"dq2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
-    for d, ti, to in FWD_INST:
-        if ti == "f32":
-            u.append(("fwd_inst.hip", f"fwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TO={to}"]))
-        di = ["-DJ_DI"] if ti == to else []  # Di launcher once per (D, dO type)
-        u.append(("bwd_inst.hip", f"bwd_{d}_{ti}_{to}", [f"-DJ_D={d}", f"-DJ_TI={ti}", f"-DJ_TG={to}"] + di))
+        u.append(("bwd_inst.hip", f"di_{d}_bf16", [f"-DJ_D={d}", "-DJ_TI=bf16", "-DJ_TG=bf16", "-DJ_DI",
+                                                   "-DJ_DI_ONLY"]))
+    for d in F32_DIMS:
+        u.append(("fwd_inst.hip", f"fwd_{d}_f32_f32", [f"-DJ_D={d}", "-DJ_TI=f32", "-DJ_TO=f32"]))
+        u.append(("bwd_inst.hip", f"bwd_{d}_f32_f32", [f"-DJ_D={d}", "-DJ_TI=f32", "-DJ_TG=f32", "-DJ_DI"]))
     return u
 
 

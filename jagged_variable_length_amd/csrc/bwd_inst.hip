@@ -1,6 +1,8 @@
 // One translation unit per (head dim, input type, gradient type) of the
-// backward kernels; compiled with -DJ_D=<32|64|128> -DJ_TI=<bf16|f32>
-// -DJ_TG=<bf16|f32>.
+// fp32-input backward kernels, compiled with -DJ_D=<32|64> -DJ_TI=f32
+// -DJ_TG=f32, plus the Di pass (-DJ_DI).  For bf16 inputs only the Di pass is
+// built from here (-DJ_DI -DJ_DI_ONLY): their dK/dV and dQ kernels are the
+// LDS-DMA ones of bwd2_inst.hip and dq2_inst.hip.
 #include "bwd_impl.hpp"
 
 #ifndef J_D
@@ -11,6 +13,7 @@ namespace jattn {
 
 typedef float f32;
 
+#ifndef J_DI_ONLY
 namespace {
 
 template <typename TI, typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT>
@@ -83,6 +86,7 @@ hipError_t JATTN_BWD_LAUNCHER(dkdv, J_D, J_TI, J_TG)(const BwdArgs& a, const Ker
   if (k.wkv == 2) return dkdv_shape<J_TI, J_TG, J_D, 2>(a, k, grid, st);
   return dkdv_shape<J_TI, J_TG, J_D, 1>(a, k, grid, st);
 }
+#endif  // J_DI_ONLY
 
 #ifdef J_DI
 // Di for this (D, dO type), both O types.

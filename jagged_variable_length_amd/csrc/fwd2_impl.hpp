@@ -170,6 +170,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
     float m_run = 0.0f, l_run = 0.0f, lr_run = 0.0f;
+    bool pad_drop = false;  // this row dropped its padded keys (see the guard below)
 
     // One K/V step.  FIRST (step 0) starts the running max at the step's
     // max; later steps rescale lazily.  Separate instances keep the
@@ -238,6 +239,29 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           p[i] = fmaf(sacc[i], a.scale_log2, c);
         }
         if constexpr (WIN) mask(p, -INFINITY);
+        if constexpr (!WIN) {
+          // Guard of the subtraction scheme.  Keys past the sample end score
+          // 0 in this last step.  When the row's best valid score is below 0
+          // (log2 units), their exp terms would dominate the row sum and the
+          // epilogue's subtraction would recover the true sum only through
+          // cancellation (or not at all once the valid terms underflow).
+          // Such rows drop the padded keys here (p = 0) and skip the
+          // subtraction.  The test uses a lower bound of the row's best score
+          // (earlier steps reach at least m_run), so it errs towards dropping,
+          // which is exact too.
+          const int rem = cur.s.lk - key0;  // valid keys of this wave's 32-key block
+          if (t + 1 == n && rem > 0 && rem < 32) {
+            float vm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vm = (BIAS ? 16 * g + i : acc_row(i, g)) < rem ? fmaxf(vm, p[i]) : vm;
+            vm = wave_xor32_max(vm);
+            pad_drop = (FIRST ? vm : m_run + fmaxf(vm, 0.0f)) < 0.0f;
+            if (pad_drop) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) p[i] = (BIAS ? 16 * g + i : acc_row(i, g)) < rem ? p[i] : -INFINITY;
+            }
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, p[i]);
         mx = wave_xor32_max(mx);
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         // masks them instead; its running max may sit at kNoScore, where
         // 2^-m overflows.)
         int npad = 0;
-        if (n > 0) npad = 32 - min(max(cur.s.lk - ((n - 1) * BN + wk * 32), 0), 32);
+        if (n > 0 && !pad_drop) npad = 32 - min(max(cur.s.lk - ((n - 1) * BN + wk * 32), 0), 32);
         const float pad_e = fast_exp2(-m_run);
         l_run -= (float)npad * pad_e;
         lr_run -= (float)npad * (float)(bf16)pad_e;

@@ -84,13 +84,8 @@ struct KernelSel {
 #define JATTN_DECLARE_FWD(D, TI, TO) \
   hipError_t JATTN_FWD_LAUNCHER(D, TI, TO)(const FwdArgs&, const KernelSel&, int, hipStream_t);
 
-JATTN_DECLARE_FWD(128, bf16, bf16)
-JATTN_DECLARE_FWD(128, bf16, f32)
-JATTN_DECLARE_FWD(64, bf16, bf16)
-JATTN_DECLARE_FWD(64, bf16, f32)
+// fp32 inputs (first-generation kernels); bf16 inputs use launch_fwd2_* below
 JATTN_DECLARE_FWD(64, f32, f32)
-JATTN_DECLARE_FWD(32, bf16, bf16)
-JATTN_DECLARE_FWD(32, bf16, f32)
 JATTN_DECLARE_FWD(32, f32, f32)
 
 #define JATTN_BWD_LAUNCHER_(K, D, TI, TG) launch_##K##_##D##_##TI##_##TG
@@ -99,13 +94,8 @@ JATTN_DECLARE_FWD(32, f32, f32)
   hipError_t JATTN_BWD_LAUNCHER(dq, D, TI, TG)(const BwdArgs&, const KernelSel&, int, hipStream_t);   \
   hipError_t JATTN_BWD_LAUNCHER(dkdv, D, TI, TG)(const BwdArgs&, const KernelSel&, int, hipStream_t);
 
-JATTN_DECLARE_BWD(128, bf16, bf16)
-JATTN_DECLARE_BWD(128, bf16, f32)
-JATTN_DECLARE_BWD(64, bf16, bf16)
-JATTN_DECLARE_BWD(64, bf16, f32)
+// fp32 inputs; bf16 inputs use launch_dkdv2_* / launch_dq2_* below
 JATTN_DECLARE_BWD(64, f32, f32)
-JATTN_DECLARE_BWD(32, bf16, bf16)
-JATTN_DECLARE_BWD(32, bf16, f32)
 JATTN_DECLARE_BWD(32, f32, f32)
 
 #define JATTN_DI_LAUNCHER_(D, TI) launch_di_##D##_##TI

@@ -64,6 +64,31 @@ def check(got, ref, name, tol=TOL):
     return err
 
 
+def check_full(got, ref, name, starts, tol=TOL, unit="row"):
+    """Every element of a full-size tensor against the oracle; prints the
+    worst error and the sample it sits in.  ``starts``: the sample offsets
+    along the first axis (rows of [T, H, D] or [T, H], or flat elements of
+    dBias).  -inf (LSE of a row without keys) must match exactly."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    inf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf), f"{name}: -inf pattern differs"
+    with np.errstate(invalid="ignore"):
+        diff = np.where(inf, 0.0, np.abs(got - ref))
+    assert np.all(np.isfinite(diff)), f"{name}: non-finite values"
+    if diff.size == 0:
+        say(f"  {name:6s} (empty)")
+        return 0.0
+    flat = int(np.argmax(diff))
+    err = float(diff.reshape(-1)[flat])
+    pos = int(np.unravel_index(flat, ref.shape)[0])
+    sample = int(np.searchsorted(np.asarray(starts), pos, side="right") - 1)
+    rms = float(np.sqrt(np.mean(np.where(inf, 0.0, ref) ** 2)))
+    say(f"  {name:6s} max|err| = {err:.3e} at sample {sample} ({unit} {pos - int(starts[sample])}), "
+        f"{diff.size} elements (rms ref {rms:.3e}, tol {tol})")
+    assert err <= tol, f"{name}: max abs error {err} > {tol} (sample {sample})"
+    return err
+
+
 def check_dbias(got, ref, name="dBias", tol=TOL):
     """dBias against the 2e-2 bound and also against its own scale: dBias
     elements shrink with the number of keys (about 1e-3 on long samples), so

@@ -33,3 +33,23 @@ def test_dbias_check_rejects_misplaced_values(shift):
     assert np.max(np.abs(planted - ref)) < 2e-2  # within the absolute bound
     with pytest.raises(AssertionError):
         check_dbias(planted, ref)
+
+
+def test_full_check_names_the_sample_of_a_planted_error(capsys):
+    """check_full compares every element and reports the sample that holds the
+    worst error (mistake planted in oracle output on the CPU)."""
+    from gpu_util import check_full
+
+    inp = gen.make_custom([5, 0, 7, 3], [4, 2, 9, 0], 2, 8, "f32", seed=1)
+    o, lse = ora.forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_offsets, inp.kv_offsets)
+    check_full(o.copy(), o, "O", inp.q_offsets)
+    check_full(lse.copy(), lse, "lse", inp.q_offsets)  # -inf rows of the keyless sample
+    bad = o.copy()
+    bad[inp.q_offsets[2] + 4, 1, 3] += 0.05  # sample 2, row 4
+    with pytest.raises(AssertionError, match="sample 2"):
+        check_full(bad, o, "O", inp.q_offsets)
+    assert "at sample 2 (row 4)" in capsys.readouterr().out
+    bad_lse = lse.copy()
+    bad_lse[inp.q_offsets[3], 0] = 0.0  # a -inf row made finite
+    with pytest.raises(AssertionError, match="-inf pattern"):
+        check_full(bad_lse, lse, "lse", inp.q_offsets)

@@ -158,3 +158,32 @@ def test_fwd_bwd_adversarial_negative_bias(lq):
     rg = oracle_bwd(inp, op)
     for name, g, r in zip(["dQ", "dK", "dV", "dBias"], (dq, dk, dv, db), rg):
         (check_dbias if name == "dBias" else check)(A.to_f64(g), r, name)
+
+
+@pytest.mark.parametrize("level", [-20.0, -1.0e4])
+@pytest.mark.parametrize("D,lq", [(64, [3, 40, 17, 1, 33, 8]), (128, [300, 64, 1, 129, 40, 200]),
+                                  (64, [300, 64, 1, 129, 40, 200])])
+def test_fwd_bwd_very_negative_bias(level, D, lq):
+    """Rows whose every valid score lies far below zero, on samples whose key
+    count is not a multiple of 32 (so the last key step holds zero-filled
+    keys scoring 0).  Softmax is shift-invariant, so the oracle's result is
+    an ordinary attention; the forward must not let the padded keys' exp
+    terms swamp the row sum (at -20 the subtraction alone would cancel to a
+    wrong sum, at -1e4 the valid terms underflow and it would give NaN): such
+    rows drop the padded keys in that step instead of subtracting them."""
+    say(f"case: very negative bias {level} D={D} lq={lq}")
+    lk = [1, 45, 31, 100, 33, 70]
+    inp = gen.make_custom(lq, lk, 2, D, "bf16", seed=29, bias=True)
+    rng = np.random.default_rng(29)
+    inp.bias = gen.f32_to_bf16_bits((level + 0.25 * rng.standard_normal(inp.bias.shape)).astype(np.float32))
+    op = make_op(inp, bias=True, want_dbias=True, out_dtype="f32", grad_dtype="f32", split=True)
+    d = device_inputs(inp)
+    o, lse = op.forward(d["q"], d["k"], d["v"], bias=d["bias"])
+    dq, dk, dv, db = op.backward(d["q"], d["k"], d["v"], d["dout"], o=o, lse=lse, bias=d["bias"])
+    sync()
+    ro, rl = oracle_fwd(inp, op)
+    check(A.to_f64(o), ro, "O")
+    check_lse(A.to_f64(lse), rl)
+    rg = oracle_bwd(inp, op)
+    for name, g, r in zip(["dQ", "dK", "dV", "dBias"], (dq, dk, dv, db), rg):
+        (check_dbias if name == "dBias" else check)(A.to_f64(g), r, name)

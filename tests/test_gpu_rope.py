@@ -13,11 +13,12 @@ import torch
 from jagged_variable_length_amd import attention as A
 from jagged_variable_length_amd import inputs as gen
 from oracle import attention as ora
+from oracle import batched as bat
 from oracle import rope
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, device_inputs, say, sync  # noqa: E402
+from gpu_util import check, check_full, device_inputs, say, sync  # noqa: E402
 
 
 def _run(inp, D, out, grad, base=0.0):
@@ -87,12 +88,16 @@ def test_block_rope_base_and_long_positions():
             check(g[rows], r, name)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_block_rope_workload_full_size():
-    """Full-size workload in the benchmark's configuration: sampled blocks,
-    each checked as its own 64-row problem at its true positions."""
+    """Full-size workload in the benchmark's configuration, every element:
+    the oracle rotates Q and K at their true positions, runs every 64-token
+    block as its own problem (oracle.batched, pinned on the CPU) and rotates
+    dQ and dK back."""
     cfg = 7
     w = gen.WORKLOADS[cfg]
-    say(f"case: workload {cfg} ({w.name}) full size")
+    say(f"case: workload {cfg} ({w.name}) full size, every element")
     inp = gen.make_inputs(cfg, cfg)
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, block_diagonal=True, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, rope=True).upload()
@@ -106,12 +111,14 @@ def test_block_rope_workload_full_size():
         assert torch.isfinite(a_).all()
         assert torch.equal(a_, b_)
     got = [A.to_f64(t) for t in outs[0]]
-    rng = np.random.default_rng(cfg)
-    picks = sorted({0, int(np.argmax(inp.lq)), int(rng.integers(0, inp.B))})
-    for b in picks:
-        nblk = (int(inp.lq[b]) + 63) // 64
-        for t in sorted({0, nblk - 1, int(rng.integers(0, nblk))}):
-            say(f"  sample {b} block {t}")
-            rows, ref = _block_oracle(inp, b, t, w.D, op.scale)
-            for name, g, r in zip(("O", "dQ", "dK", "dV"), got, ref):
-                check(g[rows], r, name)
+    del outs, d
+    off = inp.q_offsets
+    qr, kr = rope.forward(inp.f64("q"), off), rope.forward(inp.f64("k"), off)
+    v, do = inp.f64("v"), inp.f64("dout")
+    ro, _ = bat.forward(qr, kr, v, off, off, scale=op.scale, block_diagonal=True)
+    check_full(got[0], ro, "O", off)
+    del ro
+    dqr, dkr, dv, _ = bat.backward(qr, kr, v, do, off, off, scale=op.scale, block_diagonal=True)
+    check_full(got[1], rope.backward(dqr, off), "dQ", off)
+    check_full(got[2], rope.backward(dkr, off), "dK", off)
+    check_full(got[3], dv, "dV", off)
