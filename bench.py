@@ -194,15 +194,104 @@ def _window_pairs(n, window):
     return sum(min(n - 1, i + right) - max(0, i - left) + 1 for i in range(n))
 
 
+def host_info():
+    """(BLAS threads, {cpu model, BLAS vendor and version, usable cores}) of
+    the process running the oracle."""
+    cores, host = None, {}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        cores = max([t.get("num_threads", 1) for t in blas] or [1])
+        if blas:
+            host["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    host["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        host["usable_cores"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return cores, host
+
+
+class ClockSampler:
+    """Samples the shader clock the driver reports (the active level of
+    pp_dpm_sclk of the card in use) while the timed steps run."""
+
+    def __init__(self, torch):
+        self.path, self.samples, self._stop = None, [], False
+        try:
+            bus = str(torch.cuda.get_device_properties(0).pci_bus_id).lower()
+            dom = int(getattr(torch.cuda.get_device_properties(0), "pci_domain_id", 0))
+            slot = f"{dom:04x}:{bus:>02}" if len(bus) <= 2 else bus
+        except Exception:
+            slot = None
+        drm = "/sys/class/drm"
+        try:
+            cards = sorted(c for c in os.listdir(drm) if c.startswith("card") and c[4:].isdigit())
+        except OSError:
+            cards = []
+        for c in cards:
+            dev = os.path.join(drm, c, "device")
+            try:
+                with open(os.path.join(dev, "uevent")) as fh:
+                    ue = fh.read().lower()
+            except OSError:
+                continue
+            if slot is None or (f"pci_slot_name={slot}" in ue or (":" + slot.split(":")[-1] + ":00.0") in ue):
+                if os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                    self.path = os.path.join(dev, "pp_dpm_sclk")
+                    break
+
+    def _read(self):
+        with open(self.path) as fh:
+            for line in fh:
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is None:
+            return self
+
+        def run():
+            while not self._stop:
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except (OSError, ValueError, IndexError):
+                    return
+                time.sleep(0.005)
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop = True
+        if self.path is not None:
+            self._t.join(timeout=1.0)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"sclk_mhz_median": float(np.median(self.samples)), "sclk_mhz_min": float(np.min(self.samples)),
+                "sclk_mhz_max": float(np.max(self.samples)), "samples": len(self.samples)}
+
+
 def cpu_baseline(w, inp, budget_s):
     """fp64 oracle, fwd+bwd, samples in order until the time budget is spent
     (shortest first for the sliding-window workload, whose samples are long)."""
     from oracle import attention as ora
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:
-        cores = None
+    cores, host = host_info()
     q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
     do, bias = inp.f64("dout"), inp.f64("bias")
     scale = 1.0 / np.sqrt(w.D) if w.scale is None else w.scale
@@ -216,14 +305,19 @@ def cpu_baseline(w, inp, budget_s):
     ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, int(order[0]), scale=scale, activation=w.act,
                        block_diagonal=w.block_diagonal, bias=bias, window=w.window)
     flops, n, done = 0.0, 0, []
+    t_fwd = t_bwd = 0.0
     t0 = time.perf_counter()
     for b in order:
         b = int(b)
+        ta = time.perf_counter()
         ora.forward_sample(q, k, v, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
                            block_diagonal=w.block_diagonal, bias=bias, window=w.window)
+        tb = time.perf_counter()
         ora.backward_sample(q, k, v, do, inp.q_offsets, inp.kv_offsets, b, scale=scale, activation=w.act,
                             block_diagonal=w.block_diagonal, bias=bias, want_dbias=w.want_dbias,
                             window=w.window)
+        t_fwd += tb - ta
+        t_bwd += time.perf_counter() - tb
         done.append(b)
         if w.block_diagonal:
             pairs = sum(min(64, int(lq[b]) - s) ** 2 for s in range(0, int(lq[b]), 64))
@@ -238,14 +332,19 @@ def cpu_baseline(w, inp, budget_s):
     dt = time.perf_counter() - t0
     which = f"samples 0..{n - 1}" if w.window is None else \
         f"the {n} shortest samples (lengths {int(lq[done[0]])}..{int(lq[done[-1]])})"
+    f_fwd = flops / 3.5
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{which} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s"}
+            "sample": f"{which} of {inp.B} (all {w.H} heads), fwd+bwd in float64, {dt:.1f} s",
+            "fwd_s": round(t_fwd, 3), "bwd_s": round(t_bwd, 3),
+            "fwd_tflops": f_fwd / max(t_fwd, 1e-9) / 1e12, "bwd_tflops": 2.5 * f_fwd / max(t_bwd, 1e-9) / 1e12,
+            **host}
 
 
 def _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores):
     """QK-norm, attention and both backwards per sample, in float64."""
     from oracle import attention as ora
     from oracle import qknorm as qn
+    _, host = host_info()
     flops, n = 0.0, 0
     t0 = time.perf_counter()
     for b in range(inp.B):
@@ -264,13 +363,14 @@ def _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), QK-norm + attention, fwd+bwd in "
-                      f"float64, {dt:.1f} s"}
+                      f"float64, {dt:.1f} s", **host}
 
 
 def _cpu_baseline_rope(w, inp, q, k, v, do, scale, budget_s, cores):
     """RoPE, block attention and both backwards per sample, in float64."""
     from oracle import attention as ora
     from oracle import rope
+    _, host = host_info()
     flops, n = 0.0, 0
     t0 = time.perf_counter()
     for b in range(inp.B):
@@ -289,7 +389,7 @@ def _cpu_baseline_rope(w, inp, q, k, v, do, scale, budget_s, cores):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"samples 0..{n - 1} of {inp.B} (all {w.H} heads), RoPE + block attention, fwd+bwd in "
-                      f"float64, {dt:.1f} s"}
+                      f"float64, {dt:.1f} s", **host}
 
 
 def main():
@@ -378,18 +478,26 @@ def main():
     torch.cuda.synchronize()
 
     ev = {n: [] for n, _ in launches}
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        for n, f in launches:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            f()
-            b.record()
-            ev[n].append((a, b))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in lst])) for n, lst in ev.items()}
+    step_ev = []
+    clock = ClockSampler(torch)
+    with clock:
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            s0 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for n, f in launches:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                f()
+                b.record()
+                ev[n].append((a, b))
+            step_ev.append((s0, b))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    times = {n: [a.elapsed_time(b) for a, b in lst] for n, lst in ev.items()}
+    ms = {n: float(np.mean(t)) for n, t in times.items()}
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
 
     F = float(op.info.flops_fwd)
     total_flops = 3.5 * F
@@ -419,9 +527,14 @@ def main():
     kernels = {}
     for n in ms:
         b_, f_ = work[n]
-        kernels[n] = {"ms": round(ms[n], 4), "GB/s": round(b_ / (ms[n] * 1e-3) / 1e9, 1),
+        kernels[n] = {"ms": round(ms[n], 4), "ms_median": round(float(np.median(times[n])), 4),
+                      "ms_min": round(float(np.min(times[n])), 4), "GB/s": round(b_ / (ms[n] * 1e-3) / 1e9, 1),
                       "TFLOP/s": round(f_ / (ms[n] * 1e-3) / 1e12, 2)}
 
+    clk = clock.summary()
+    if clk:
+        # the dense bf16 MFMA peak at the sampled clock: 256 CU x 4096 FLOP/clk
+        roof["peak_at_sampled_clock_tflops"] = round(256 * 4096 * clk["sclk_mhz_median"] * 1e6 / 1e12, 1)
     out = {
         "metric": "jagged attn fwd+bwd TFLOPs (valid tokens) and % of bf16 MFMA peak, 1 GPU",
         "value": round(value, 3),
@@ -431,6 +544,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_events": {"median": round(float(np.median(step_ms)), 4), "min": round(float(np.min(step_ms)), 4),
+                               "mean": round(float(np.mean(step_ms)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -448,6 +563,7 @@ def main():
                    "dbias_dtype": w.dbias_dtype if w.want_dbias else None},
         "kernels": kernels,
         "roofline": roof,
+        "clock": clock.summary(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

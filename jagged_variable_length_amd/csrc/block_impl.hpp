@@ -309,7 +309,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_fwd_kernel(FwdArgs a) {
           sacc[kb][qb][i] = e;
           ls += e;
         }
-      ls = wave_xor32_sum(ls) - (float)npad * round_p<bf16>(exp2f(-mx));
+      // (a full block has no padded keys; its max may sit far below zero,
+      // where 2^-m overflows and 0 * inf would be NaN)
+      ls = wave_xor32_sum(ls) - (npad > 0 ? (float)npad * round_p<bf16>(exp2f(-mx)) : 0.0f);
       const float inv = 1.0f / ls;
       f32x16 oacc[ND];
 #pragma unroll
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void block_bwd_kernel(BwdArgs a) {
           sacc[kb][i] = e;
           ls += e;
         }
-      ls = wave_xor32_sum(ls) - (float)npad * exp2f(-mx);
+      ls = wave_xor32_sum(ls) - (npad > 0 ? (float)npad * exp2f(-mx) : 0.0f);
       const float inv = 1.0f / ls;
       // Di = sum_j P_ij dP_ij over the block's keys (tail keys have dP = 0)
       float di = 0.0f;

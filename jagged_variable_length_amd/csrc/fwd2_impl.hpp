@@ -349,9 +349,13 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         // 2^-m overflows.)
         int npad = 0;
         if (n > 0 && !pad_drop) npad = 32 - min(max(cur.s.lk - ((n - 1) * BN + wk * 32), 0), 32);
-        const float pad_e = fast_exp2(-m_run);
-        l_run -= (float)npad * pad_e;
-        lr_run -= (float)npad * (float)(bf16)pad_e;
+        // (only when there are padded keys: a row without them may sit far
+        // below zero, where 2^-m overflows and 0 * inf would be NaN)
+        if (npad > 0) {
+          const float pad_e = fast_exp2(-m_run);
+          l_run -= (float)npad * pad_e;
+          lr_run -= (float)npad * (float)(bf16)pad_e;
+        }
       }
       if (cur.s.lk <= wk * 32) {
         // this wave's key block lies wholly past the sample end: it holds no

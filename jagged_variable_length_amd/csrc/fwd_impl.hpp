@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < ND; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY;  // running max (log2 units), softmax only
+    bool pad_drop = false;    // the row dropped its padded keys (guard above the epilogue)
     float l_run = 0.0f;       // this lane's partial row sum (exact P, for LSE)
     float lr_run = 0.0f;      // same with P as the PV product sees it (for O)
 
@@ -265,6 +266,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
             mx = fmaxf(mx, x);
           }
         }
+        if (t + 1 == ntiles) {
+          // Guard of the subtraction scheme: keys past the sample end score 0
+          // in this last tile; a row whose best valid score is below 0 drops
+          // them (p = 0) instead of subtracting their exp terms later, which
+          // would cancel (or give NaN once the valid terms underflow).
+          const int valid_w = s.lk - (t * BN + wk * NBW * 32);  // valid keys of this wave's blocks
+          if (valid_w > 0 && valid_w < NBW * 32) {
+            float vm = -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) vm = nb * 32 + acc_row(i, g) < valid_w ? fmaxf(vm, p[nb][i]) : vm;
+            vm = wave_xor32_max(vm);
+            pad_drop = fmaxf(m_run, vm) < 0.0f;
+            if (pad_drop) {
+              mx = -INFINITY;
+#pragma unroll
+              for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  p[nb][i] = nb * 32 + acc_row(i, g) < valid_w ? p[nb][i] : -INFINITY;
+                  mx = fmaxf(mx, p[nb][i]);
+                }
+            }
+          }
+        }
         mx = wave_xor32_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2f(m_run - m_new);
@@ -342,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     if constexpr (SOFTMAX) {
       // keys past the sample end read as zero: each adds exp2(0 - m) to l
       int npad = 0;
-      if (ntiles > 0) {
+      if (ntiles > 0 && !pad_drop) {
         const int last0 = (ntiles - 1) * BN;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
@@ -351,9 +378,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
           npad += 32 - valid;
         }
       }
-      const float pad_e = exp2f(-m_run);
+      // (only with padded keys: without them m may sit far below zero, where
+      // 2^-m overflows and 0 * inf would be NaN)
+      const float pad_e = npad > 0 ? exp2f(-m_run) : 0.0f;
       l_run = wave_xor32_sum(l_run) - (float)npad * pad_e;
       lr_run = wave_xor32_sum(lr_run) - (float)npad * round_p<TI>(pad_e);
+      if (WK > 1 && s.lk <= wk * NBW * 32) {
+        // this wave's key blocks lie wholly past the sample end: it holds no
+        // term of the row (its zero scores must not set the combined max)
+        m_run = -INFINITY;
+        l_run = 0.0f;
+        lr_run = 0.0f;
+      }
       if constexpr (WK == 1) {
         scale_out = (s.lk > 0) ? 1.0f / lr_run : 0.0f;
         lse2 = (s.lk > 0) ? m_run + __log2f(l_run) : -INFINITY;
