@@ -238,6 +238,28 @@ int jattn_bwd_stages(const jattn_plan* plan, int32_t stages, const void* q, cons
                      const void* dout, void* dq, void* dk, void* dv, void* dbias, void* workspace,
                      void* stream);
 
+/* Backward with a fixed scratch: the same computation, kernels and results
+ * as jattn_bwd (all stages), for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The row statistics that jattn_bwd keeps in the workspace's
+ * scratch region (Di and LSE * log2 e, 2 * align256(4 Tq H) bytes) live
+ * instead in a fixed device array of the library, 32 MiB per GPU, held from
+ * the first call on that GPU until the process ends; the call itself
+ * allocates nothing.  `workspace` must still hold the uploaded plan
+ * (jattn_plan_upload), which is only read; its scratch region is not
+ * touched.  The array is found on the current device: `stream` must belong
+ * to it (JATTN_E_ARG otherwise).  Plans whose row statistics exceed 32 MiB
+ * (softmax without the block mask and Tq * H above about 4.19 million rows)
+ * are refused with JATTN_E_WORKSPACE before anything is enqueued; GDPA and
+ * block-mode plans use no row statistics and have no such limit.  Every call
+ * on one GPU shares that GPU's array: two calls whose kernels overlap on
+ * the same GPU (on unordered streams) race on it.  Each call overwrites the
+ * rows it reads before reading them, so nothing needs clearing between
+ * calls. */
+int jattn_bwd_fixed_scratch(const jattn_plan* plan, const void* q, const void* k, const void* v,
+                            const void* bias, const void* o, const float* lse, const void* dout, void* dq,
+                            void* dk, void* dv, void* dbias, void* workspace, void* stream);
+
 void jattn_plan_destroy(jattn_plan* plan);
 
 /* QK-norm ("Training GEM at LLM scale", section "Generalized Dot-Product

@@ -26,8 +26,8 @@ JATTN_PLAN_FWD, JATTN_PLAN_DKDV, JATTN_PLAN_DQ, JATTN_PLAN_BLOCK = 0, 1, 2, 3
 JATTN_BWD_PREP, JATTN_BWD_DKDV, JATTN_BWD_DQ, JATTN_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
-            "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_plan_destroy", "jattn_strerror",
-            "jattn_last_error", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]
+            "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_bwd_fixed_scratch", "jattn_plan_destroy",
+            "jattn_strerror", "jattn_last_error", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]
 
 
 class JattnError(RuntimeError):
@@ -80,6 +80,7 @@ def lib():
     L.jattn_fwd.argtypes = [vp] * 9
     L.jattn_bwd.argtypes = [vp] * 14
     L.jattn_bwd_stages.argtypes = [vp, i32] + [vp] * 13
+    L.jattn_bwd_fixed_scratch.argtypes = [vp] * 14
     L.jattn_plan_destroy.argtypes = [vp]
     L.jattn_plan_destroy.restype = None
     L.jattn_strerror.argtypes = [ctypes.c_int]
@@ -89,7 +90,8 @@ def lib():
     L.jattn_l2norm_fwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
     L.jattn_l2norm_bwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, vp]
     for name in ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
-                 "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]:
+                 "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_bwd_fixed_scratch", "jattn_l2norm_fwd",
+                 "jattn_l2norm_bwd"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -143,6 +145,10 @@ def jattn_bwd(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, s
 
 def jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
     _check(lib().jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
+
+
+def jattn_bwd_fixed_scratch(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
+    _check(lib().jattn_bwd_fixed_scratch(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
 
 
 def jattn_l2norm_fwd(x, y, rnorm, rows, D, x_dtype, y_dtype, stream) -> None:

@@ -38,7 +38,7 @@ BF16_DIMS = (128, 64, 32)
 def units():
     """(source, object name, extra defines) of every translation unit."""
     u = [("api.cpp", "api", []), ("planner.cpp", "planner", []), ("block_inst.hip", "block", []),
-         ("l2norm.hip", "l2norm", [])]
+         ("l2norm.hip", "l2norm", []), ("fixed_scratch.hip", "fixed_scratch", [])]
     for d in BF16_DIMS:
         u.append(("fwd2_inst.hip", f"fwd2_{d}", [f"-DJ_D={d}"]))
         for tg in ("bf16", "f32"):

@@ -85,6 +85,10 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(JATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, const void* v, const void* bias,
+            const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias,
+            void* workspace, void* stream, bool fixed_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -405,11 +409,37 @@ int jattn_bwd(const jattn_plan* p, const void* q, const void* k, const void* v, 
 int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const void* k, const void* v,
                      const void* bias, const void* o, const float* lse, const void* dout, void* dq, void* dk,
                      void* dv, void* dbias, void* workspace, void* stream) {
+  return bwd_run(p, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream, false);
+}
+
+int jattn_bwd_fixed_scratch(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias,
+                            const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* dbias, void* workspace, void* stream) {
+  return bwd_run(p, JATTN_BWD_ALL, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Row-statistics region (Di, then LSE * log2 e, each Tq * H floats) of a
+// backward: in the workspace after the plan, or at the start of the library's
+// fixed device scratch.
+int64_t rowstat_bytes(const jattn_plan* p) { return 2 * align_up(p->Tq * p->H * 4, 256); }
+
+int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, const void* v, const void* bias,
+            const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias,
+            void* workspace, void* stream, bool fixed_scratch) {
   if (!p) return fail(JATTN_E_NULL, "null plan");
   if (stages < 0 || stages > JATTN_BWD_ALL) return fail(JATTN_E_ARG, "unknown backward stage mask");
-  if (p->Tq == 0 && p->Tk == 0) return ok();
   // softmax outside block mode keeps row statistics from the forward
   const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask != JATTN_MASK_BLOCKDIAG64;
+  if (fixed_scratch && softmax_dense && rowstat_bytes(p) > (int64_t)jattn::fixed_scratch_bytes())
+    return fail(JATTN_E_WORKSPACE, "the row statistics of this plan (" + std::to_string(rowstat_bytes(p)) +
+                                       " bytes, Tq * H = " + std::to_string(p->Tq * p->H) +
+                                       ") exceed the fixed scratch of " +
+                                       std::to_string(jattn::fixed_scratch_bytes()) + " bytes");
+  if (p->Tq == 0 && p->Tk == 0) return ok();
   if ((p->Tq > 0 && (!q || !dout || !dq)) || (p->Tk > 0 && (!k || !v || !dk || !dv)))
     return fail(JATTN_E_NULL, "null q/k/v/dout/dq/dk/dv");
   if (p->desc.has_bias && !bias && p->bias_elems > 0) return fail(JATTN_E_NULL, "bias required (has_bias = 1)");
@@ -428,6 +458,23 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
 
   float* di = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->di_off);
   float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lse2_off);
+  if (fixed_scratch && softmax_dense && p->Tq > 0) {
+    // the current device's copy of the fixed scratch; the stream must belong
+    // to that device
+    if (st != nullptr) {
+      int sdev = -1, cdev = -1;
+      hipError_t e = hipStreamGetDevice(st, &sdev);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+      e = hipGetDevice(&cdev);
+      if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+      if (sdev != cdev) return fail(JATTN_E_ARG, "the stream belongs to another device than the current one");
+    }
+    void* base = nullptr;
+    const hipError_t e = jattn::fixed_scratch_address(&base);
+    if (e != hipSuccess) return hip_fail(e, "fixed scratch address (hipGetSymbolAddress)");
+    di = reinterpret_cast<float*>(base);
+    lse2 = reinterpret_cast<float*>(static_cast<char*>(base) + align_up(p->Tq * p->H * 4, 256));
+  }
   KernelSel sel = base_sel(p);
   sel.out_f32 = p->desc.grad_dtype == JATTN_F32;
   sel.wq = p->dq_wq;
@@ -493,6 +540,10 @@ int jattn_bwd_stages(const jattn_plan* p, int32_t stages, const void* q, const v
   }
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 void jattn_plan_destroy(jattn_plan* p) { delete p; }
 

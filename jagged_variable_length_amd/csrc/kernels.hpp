@@ -137,6 +137,11 @@ hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_
 hipError_t launch_block_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_block_bwd(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 
+// Fixed device scratch (fixed_scratch.hip): its size, and its address on the
+// current device (looked up on the first call per device, then kept).
+size_t fixed_scratch_bytes();
+hipError_t fixed_scratch_address(void** out);
+
 // QK-norm (row-wise L2 normalisation) of `rows` rows of D elements
 hipError_t launch_l2norm_fwd(const void* x, void* y, float* rnorm, int64_t rows, int D, bool x_f32, bool y_f32,
                              hipStream_t st);
