@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2   # dense MXFP8 / FP8 MFMA: twice the bf16 rate
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -63,7 +64,7 @@ def copy_calibration(mib, steps):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
-def kernel_work(w, info, es_in, es_out, es_g, es_db=4):
+def kernel_work(w, info, es_in, es_out, es_g, es_db=4, mx=None):
     """Algorithmic bytes and FLOPs of each launch (every interface tensor once)."""
     H, D = w.H, w.D
     Tq, Tk, nb = int(info.Tq), int(info.Tk), int(info.bias_elems)
@@ -76,6 +77,17 @@ def kernel_work(w, info, es_in, es_out, es_g, es_db=4):
         return {
             "block_fwd": (3 * qd * es_in + qd * es_out, F),
             "block_bwd": (4 * qd * es_in + 3 * qd * es_g, 2.5 * F),
+        }
+    if w.mxfp8:
+        # codes 1 byte per element; the transposed copies ~1 byte per element
+        # (plus the zero tails of partial 32-token blocks); scales 1/32 byte
+        nq, nk = mx  # (codes, codes_t, scales) bytes of a query-row and a key-row tensor
+        return {
+            "quant": (2 * (2 * qd + 2 * kd) + 2 * sum(nq) + 2 * sum(nk), 0.0),
+            "fwd": (nq[0] + nq[2] + nk[0] + nk[1] + 2 * nk[2] + qd * es_out + rowstat, F),
+            "prep": (nq[0] + nq[2] + qd * es_out + rowstat + 2 * rowstat, 2.0 * qd),
+            "dkdv": (2 * sum(nq) + nk[0] + nk[0] + 2 * nk[2] + 2 * rowstat + 2 * kd * es_g, 2.0 * F),
+            "dq": (2 * (nq[0] + nq[2]) + sum(nk) + nk[0] + nk[2] + 2 * rowstat + qd * es_g, 0.5 * F),
         }
     soft = w.act == "softmax"
     work = {
@@ -295,6 +307,12 @@ def cpu_baseline(w, inp, budget_s):
     q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
     do, bias = inp.f64("dout"), inp.f64("bias")
     scale = 1.0 / np.sqrt(w.D) if w.scale is None else w.scale
+    if w.mxfp8:
+        # the MXFP8 oracle: the definition on the block-quantised values
+        # (quantisation itself done before the timed samples)
+        from oracle import mxfp8 as mx
+        q, do = mx.quantize(q, inp.q_offsets)[2], mx.quantize(do, inp.q_offsets)[2]
+        k, v = mx.quantize(k, inp.kv_offsets)[2], mx.quantize(v, inp.kv_offsets)[2]
     if w.qk_norm:
         return _cpu_baseline_qknorm(w, inp, q, k, v, do, scale, budget_s, cores)
     if w.rope:
@@ -415,7 +433,8 @@ def main():
     w = gen.WORKLOADS[cfg]
     inp = gen.make_inputs(cfg)  # the workload's canonical seed
     op = A.JaggedAttention(inp.q_offsets, inp.kv_offsets, w.H, w.D, act=w.act, block_diagonal=w.block_diagonal,
-                           has_bias=w.bias, want_dbias=w.want_dbias, in_dtype=w.dtype, out_dtype=w.out_dtype,
+                           has_bias=w.bias, want_dbias=w.want_dbias,
+                           in_dtype="mxfp8" if w.mxfp8 else w.dtype, out_dtype=w.out_dtype,
                            grad_dtype=w.grad_dtype, split_operands=w.split_operands, order=args.order,
                            num_workers=args.workers, dbias_dtype=w.dbias_dtype, window=w.window,
                            scale=w.scale, rope=w.rope)
@@ -446,7 +465,25 @@ def main():
     plan_ms = (time.perf_counter() - t1) * 1e3
     Bd.jattn_plan_destroy(p2)
 
-    if w.block_diagonal:
+    if w.mxfp8:
+        # the step starts from bf16 Q, K, V, dO: quantisation (the upstream
+        # producer's job in the pages' design) is timed as part of it
+        mq, mk, mv, mdo = op.mx_empty("q"), op.mx_empty("kv"), op.mx_empty("kv"), op.mx_empty("q")
+        mx_sizes = (Bd.jattn_mx_sizes(op.plan, Bd.JATTN_MX_Q), Bd.jattn_mx_sizes(op.plan, Bd.JATTN_MX_KV))
+
+        def quant():
+            op.mx_quantize(dev["q"], "q", out=mq)
+            op.mx_quantize(dev["k"], "kv", out=mk)
+            op.mx_quantize(dev["v"], "kv", out=mv)
+            op.mx_quantize(dev["dout"], "q", out=mdo)
+
+        def mx_stage(s_):
+            return lambda: op.mx_backward(mq, mk, mv, mdo, o=o, lse=lse, dq=dq, dk=dk, dv=dv, stages=s_)
+        launches = [("quant", quant), ("fwd", lambda: op.mx_forward(mq, mk, mv, o=o, lse=lse))]
+        if w.act == "softmax":
+            launches.append(("prep", mx_stage(Bd.JATTN_BWD_PREP)))
+        launches += [("dkdv", mx_stage(Bd.JATTN_BWD_DKDV)), ("dq", mx_stage(Bd.JATTN_BWD_DQ))]
+    elif w.block_diagonal:
         launches = [("block_fwd", lambda: op.forward(dev["q"], dev["k"], dev["v"], o=o)),
                     ("block_bwd", lambda: op.backward(dev["q"], dev["k"], dev["v"], dev["dout"], dq=dq, dk=dk, dv=dv))]
     else:
@@ -503,10 +540,11 @@ def main():
     total_flops = 3.5 * F
     ms_per_step = wall * 1e3 / args.steps
     value = total_flops / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else (PEAK_FP8_TFLOPS if w.mxfp8 else PEAK_BF16_TFLOPS)
 
     es = {"bf16": 2, "f32": 4}
-    work = kernel_work(w, op.info, es[w.dtype], es[w.out_dtype], es[w.grad_dtype], es[w.dbias_dtype])
+    work = kernel_work(w, op.info, es[w.dtype], es[w.out_dtype], es[w.grad_dtype], es[w.dbias_dtype],
+                       mx=mx_sizes if w.mxfp8 else None)
     dom = max(ms, key=lambda n: ms[n])
     nbytes, nflops = work[dom]
     t = ms[dom] * 1e-3
@@ -549,13 +587,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "mxfp8" if w.mxfp8 else w.dtype,
         "data": "synthetic (seeded; lengths and value distributions of the workload)",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} D={w.D} {w.dtype} act={w.act}"
                                f"{' bias+dbias' if w.bias else ''}{' blockdiag64' if w.block_diagonal else ''}"
                                f"{f' window={w.window}' if w.window else ''}"
                                f"{f' qk-norm scale={w.scale}' if w.qk_norm else ''}"
-                               f"{' rope' if w.rope else ''}",
+                               f"{' rope' if w.rope else ''}{' mxfp8 (32x32 blocks, E4M3/E8M0)' if w.mxfp8 else ''}",
                    "workload_index": cfg, "Tq": op.Tq, "Tk": op.Tk,
                    "seed": cfg if w.seed is None else w.seed,
                    "flops_fwd": F, "flops_fwd_bwd": total_flops, "plan_ms_host": round(plan_ms, 3),

@@ -98,6 +98,8 @@ extern "C" {
 /* element types */
 #define JATTN_BF16 0
 #define JATTN_F32 1
+#define JATTN_MXFP8 2 /* desc.in_dtype only: inputs are MXFP8 tensors made by
+                         jattn_mx_quantize (see the MXFP8 section below) */
 
 /* unit order across workers (desc.order) */
 #define JATTN_HEAVY_FIRST 0 /* cost-sorted units dealt round-robin */
@@ -280,6 +282,77 @@ int jattn_l2norm_fwd(const void* x, void* y, float* rnorm, int64_t rows, int32_t
                      int32_t y_dtype, void* stream);
 int jattn_l2norm_bwd(const void* x, const void* dy, void* dx, int64_t rows, int32_t D, int32_t x_dtype,
                      int32_t dy_dtype, int32_t dx_dtype, void* stream);
+
+/* ---- MXFP8 attention --------------------------------------------------
+ * "Training GEM at LLM scale", section "Mixed Ultra-Low-Precision Training",
+ * part "Low Precision Flash Attention": the attention products run as MXFP8
+ * block-scaled matrix products; every input tensor is quantised once, with
+ * one shared power-of-two scale per square 32 x 32 block (so a block and its
+ * transpose share it), and the kernel converts P to MXFP8 itself, taking
+ * its shared exponent from the row maximum softmax already keeps.
+ *
+ * A plan with desc.in_dtype = JATTN_MXFP8 (D = 64 or 128, mask NONE, no
+ * bias, softmax / erf-GELU / SiLU) runs through the calls below; jattn_fwd
+ * and jattn_bwd refuse it.  An MXFP8 tensor of a jagged [T, H, D] bf16
+ * tensor (T = Tq for Q, Tk for K and V) is three device arrays:
+ *   codes    uint8 [T, H, D]        FP8 E4M3 codes (OCP format), row-major
+ *   codes_t  uint8 [RB, H, D, 32]   the same codes per 32-token block,
+ *                                   feature-major; tokens past a sample's
+ *                                   end are zero
+ *   scales   uint8 [RB, H, D / 32]  E8M0 byte X + 127 of each block: the
+ *                                   block's values are codes * 2^X
+ * RB = sum_b ceil(len_b / 32); blocks never straddle two samples.  X is the
+ * smallest integer with amax * 2^-X <= 448 (amax = the block's largest
+ * magnitude), so nothing saturates; elements are rounded to nearest, ties to
+ * even.  Sizes: jattn_mx_sizes.  The arrays are caller-owned; codes and
+ * codes_t 16-byte aligned, scales 4-byte aligned. */
+#define JATTN_MX_Q 0  /* rows of the query offsets (Q, dO) */
+#define JATTN_MX_KV 1 /* rows of the key/value offsets (K, V) */
+
+typedef struct {
+  void* codes;   /* uint8 [T, H, D] */
+  void* codes_t; /* uint8 [RB, H, D, 32]; may be NULL where not read */
+  void* scales;  /* uint8 [RB, H, D / 32] */
+} jattn_mx_tensor;
+
+/* Bytes of the three arrays of an MXFP8 tensor with the query (JATTN_MX_Q)
+ * or key/value (JATTN_MX_KV) rows of the plan (the scales size rounded up to
+ * a multiple of 4: the kernels read scale bytes as aligned dwords).  Host
+ * only. */
+int jattn_mx_sizes(const jattn_plan* plan, int32_t rows, int64_t* codes_bytes, int64_t* codes_t_bytes,
+                   int64_t* scales_bytes);
+
+/* Quantise a bf16 [T, H, D] tensor (16-byte aligned) into out->codes,
+ * out->scales and, when out->codes_t is not NULL, out->codes_t; `workspace`
+ * holds the uploaded plan (its block tables).  Enqueued on `stream`. */
+int jattn_mx_quantize(const jattn_plan* plan, int32_t rows, const void* x, const jattn_mx_tensor* out,
+                      void* workspace, void* stream);
+
+/* MXFP8 forward: reads q->codes, k->codes, v->codes_t and the three scale
+ * arrays; writes o (out_dtype, [Tq, H, D]) and, for softmax, lse [Tq, H]
+ * (may be NULL).  S = scale Q K^T and O = P V are MXFP8 products with fp32
+ * accumulation; P is rounded to E4M3 with one shared exponent per row and
+ * 64-key step (from the step's row maximum), or per row and 32-key block of
+ * the largest |P| for GDPA; the row sum uses the unrounded P.  Zero-length
+ * samples and the tail handling are as for jattn_fwd. */
+int jattn_mx_fwd(const jattn_plan* plan, const jattn_mx_tensor* q, const jattn_mx_tensor* k,
+                 const jattn_mx_tensor* v, void* o, float* lse, void* workspace, void* stream);
+
+/* MXFP8 backward, the stages in `stages` (JATTN_BWD_* mask, as for
+ * jattn_bwd_stages; JATTN_BWD_ALL for the whole backward): given dout as an
+ * MXFP8 tensor (JATTN_MX_Q rows) and, for softmax, o and the forward's lse,
+ * writes dq, dk, dv (grad_dtype).  Reads
+ * q and dout (codes, codes_t, scales), k (codes, codes_t, scales) and v
+ * (codes, scales).  Di = rowsum(dout * o) uses the dequantised dout.  The
+ * products S, dP, dV = P^T dO, dK = dS^T Q, dQ = dS K are MXFP8 with fp32
+ * accumulation; P is rounded to E4M3 with the fixed exponent -8 (P <= 1
+ * given the row's LSE; GDPA: one exponent per 32 x 32 block) and dS with one
+ * exponent per 32 x 32 block (query block x key block), so the dK and dQ
+ * products share its scales.  No atomics: dK/dV and dQ are separate passes.
+ * Uses the workspace's scratch region for Di and LSE * log2 e. */
+int jattn_mx_bwd(const jattn_plan* plan, int32_t stages, const jattn_mx_tensor* q, const jattn_mx_tensor* k,
+                 const jattn_mx_tensor* v, const void* o, const float* lse, const jattn_mx_tensor* dout,
+                 void* dq, void* dk, void* dv, void* workspace, void* stream);
 
 /* Static text for a status code. */
 const char* jattn_strerror(int status);

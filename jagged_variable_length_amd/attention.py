@@ -14,7 +14,7 @@ from . import binding as _b
 
 _ACT = {"softmax": _b.JATTN_SOFTMAX, "gelu": _b.JATTN_GELU_ERF, "silu": _b.JATTN_SILU,
         "gelu_poly": _b.JATTN_GELU_POLY}
-_DT = {"bf16": _b.JATTN_BF16, "f32": _b.JATTN_F32}
+_DT = {"bf16": _b.JATTN_BF16, "f32": _b.JATTN_F32, "mxfp8": _b.JATTN_MXFP8}
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 _ORDER = {"heavy_first": _b.JATTN_HEAVY_FIRST, "zigzag": _b.JATTN_ZIGZAG, "lpt": _b.JATTN_LPT}
 
@@ -44,6 +44,19 @@ def _args(*specs):
         if t is not None and t.device.type != "cuda":
             raise ValueError(f"{name}: must be a device tensor")
     return [_ptr(t) for t, _, _, _ in specs]
+
+
+class MxTensor:
+    """An MXFP8 tensor (include/jattn.h): E4M3 codes [T, H, D], the same codes
+    per 32-token block feature-major [RB, H, D, 32] (or None), and the E8M0
+    block scales [RB, H, D/32], all uint8 device tensors."""
+
+    def __init__(self, codes, codes_t, scales):
+        self.codes, self.codes_t, self.scales = codes, codes_t, scales
+
+    def c(self) -> "_b.jattn_mx_tensor":
+        return _b.jattn_mx_tensor(self.codes.data_ptr(), self.codes_t.data_ptr() if self.codes_t is not None else None,
+                                  self.scales.data_ptr())
 
 
 class JaggedAttention:
@@ -81,8 +94,8 @@ class JaggedAttention:
         self.H, self.D = H, D
         self.act = act
         self.in_dtype = in_dtype
-        self.out_dtype = out_dtype or in_dtype
-        self.grad_dtype = grad_dtype or in_dtype
+        self.out_dtype = out_dtype or ("bf16" if in_dtype == "mxfp8" else in_dtype)
+        self.grad_dtype = grad_dtype or ("bf16" if in_dtype == "mxfp8" else in_dtype)
         self.dbias_dtype = dbias_dtype or self.grad_dtype
         self.has_bias, self.want_dbias = has_bias, want_dbias
         self.block_diagonal = block_diagonal
@@ -172,6 +185,60 @@ class JaggedAttention:
         else:
             _b.jattn_bwd_stages(self.plan, stages, *args)
         return dq, dk, dv, dbias
+
+    # ---- MXFP8 ("Mixed Ultra-Low-Precision Training": low-precision attention) ----
+    def mx_empty(self, rows: str = "q", transposed: bool = True) -> MxTensor:
+        """Device buffers for an MXFP8 tensor with the plan's query ("q") or
+        key/value ("kv") rows."""
+        nc, nt, ns = _b.jattn_mx_sizes(self.plan, _b.JATTN_MX_Q if rows == "q" else _b.JATTN_MX_KV)
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        return MxTensor(torch.empty(max(nc, 16), **u8), torch.empty(max(nt, 16), **u8) if transposed else None,
+                        torch.empty(max(ns, 16), **u8))
+
+    def mx_quantize(self, x: torch.Tensor, rows: str = "q", transposed: bool = True,
+                    out: Optional[MxTensor] = None) -> MxTensor:
+        """Quantise a bf16 [T, H, D] tensor with the plan's query ("q") or
+        key/value ("kv") rows into an MXFP8 tensor (library kernel)."""
+        which = _b.JATTN_MX_Q if rows == "q" else _b.JATTN_MX_KV
+        T = self.Tq if rows == "q" else self.Tk
+        nc, nt, ns = _b.jattn_mx_sizes(self.plan, which)
+        px = _args((x, "x", "bf16", T * self.H * self.D))[0]
+        if self.workspace is None:
+            self.upload()
+        m = out if out is not None else self.mx_empty(rows, transposed)
+        if m.codes.numel() < nc or m.scales.numel() < ns or (m.codes_t is not None and m.codes_t.numel() < nt):
+            raise ValueError("MXFP8 output buffers are smaller than the plan needs")
+        _b.jattn_mx_quantize(self.plan, which, px, m.c(), self.workspace.data_ptr(), self._stream())
+        return m
+
+    def mx_forward(self, q: MxTensor, k: MxTensor, v: MxTensor, o=None, lse=None, want_lse=True):
+        """MXFP8 forward on quantised Q, K, V (q.codes, k.codes, v.codes_t)."""
+        _args((o, "o", self.out_dtype, self.Tq * self.H * self.D), (lse, "lse", "f32", self.Tq * self.H))
+        if self.workspace is None:
+            self.upload()
+        if o is None:
+            o = torch.empty(self.Tq, self.H, self.D, dtype=_TORCH_DT[self.out_dtype], device=self.device)
+        if lse is None and want_lse and self.act == "softmax":
+            lse = torch.empty(self.Tq, self.H, dtype=torch.float32, device=self.device)
+        _b.jattn_mx_fwd(self.plan, q.c(), k.c(), v.c(), _ptr(o), _ptr(lse), self.workspace.data_ptr(),
+                        self._stream())
+        return o, lse
+
+    def mx_backward(self, q: MxTensor, k: MxTensor, v: MxTensor, dout: MxTensor, o=None, lse=None, dq=None,
+                    dk=None, dv=None, stages=_b.JATTN_BWD_ALL):
+        """MXFP8 backward (include/jattn.h, jattn_mx_bwd); returns (dQ, dK, dV)."""
+        nq, nk = self.Tq * self.H * self.D, self.Tk * self.H * self.D
+        _args((o, "o", self.out_dtype, nq), (lse, "lse", "f32", self.Tq * self.H),
+              (dq, "dq", self.grad_dtype, nq), (dk, "dk", self.grad_dtype, nk), (dv, "dv", self.grad_dtype, nk))
+        if self.workspace is None:
+            self.upload()
+        gdt = _TORCH_DT[self.grad_dtype]
+        dq = dq if dq is not None else torch.empty(self.Tq, self.H, self.D, dtype=gdt, device=self.device)
+        dk = dk if dk is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
+        dv = dv if dv is not None else torch.empty(self.Tk, self.H, self.D, dtype=gdt, device=self.device)
+        _b.jattn_mx_bwd(self.plan, stages, q.c(), k.c(), v.c(), _ptr(o), _ptr(lse), dout.c(), _ptr(dq), _ptr(dk),
+                        _ptr(dv), self.workspace.data_ptr(), self._stream())
+        return dq, dk, dv
 
     def __del__(self):
         try:

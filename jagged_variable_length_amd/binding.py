@@ -19,7 +19,8 @@ JATTN_E_NULL, JATTN_E_OFFSETS, JATTN_E_SHAPE, JATTN_E_UNSUPPORTED = -1, -2, -3, 
 JATTN_E_ALIGN, JATTN_E_WORKSPACE, JATTN_E_STATE, JATTN_E_HIP, JATTN_E_ARG = -5, -6, -7, -8, -9
 JATTN_SOFTMAX, JATTN_GELU_ERF, JATTN_SILU, JATTN_GELU_POLY = 0, 1, 2, 3
 JATTN_MASK_NONE, JATTN_MASK_BLOCKDIAG64, JATTN_MASK_WINDOW = 0, 1, 2
-JATTN_BF16, JATTN_F32 = 0, 1
+JATTN_BF16, JATTN_F32, JATTN_MXFP8 = 0, 1, 2
+JATTN_MX_Q, JATTN_MX_KV = 0, 1
 JATTN_HEAVY_FIRST, JATTN_ZIGZAG, JATTN_LPT = 0, 1, 2
 JATTN_PLAN_FWD, JATTN_PLAN_DKDV, JATTN_PLAN_DQ, JATTN_PLAN_BLOCK = 0, 1, 2, 3
 
@@ -27,7 +28,8 @@ JATTN_BWD_PREP, JATTN_BWD_DKDV, JATTN_BWD_DQ, JATTN_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
             "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_bwd_fixed_scratch", "jattn_plan_destroy",
-            "jattn_strerror", "jattn_last_error", "jattn_l2norm_fwd", "jattn_l2norm_bwd"]
+            "jattn_strerror", "jattn_last_error", "jattn_l2norm_fwd", "jattn_l2norm_bwd", "jattn_mx_sizes",
+            "jattn_mx_quantize", "jattn_mx_fwd", "jattn_mx_bwd"]
 
 
 class JattnError(RuntimeError):
@@ -45,6 +47,10 @@ class jattn_desc(ctypes.Structure):
                 ("order", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("dbias_dtype", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("window_right", ctypes.c_int32), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+
+
+class jattn_mx_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("codes_t", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class jattn_kernel_plan(ctypes.Structure):
@@ -89,9 +95,14 @@ def lib():
     L.jattn_last_error.restype = ctypes.c_char_p
     L.jattn_l2norm_fwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
     L.jattn_l2norm_bwd.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, vp]
+    mxp = ctypes.POINTER(jattn_mx_tensor)
+    L.jattn_mx_sizes.argtypes = [vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.jattn_mx_quantize.argtypes = [vp, i32, vp, mxp, vp, vp]
+    L.jattn_mx_fwd.argtypes = [vp, mxp, mxp, mxp, vp, vp, vp, vp]
+    L.jattn_mx_bwd.argtypes = [vp, i32, mxp, mxp, mxp, vp, vp, mxp, vp, vp, vp, vp, vp]
     for name in ["jattn_plan_create", "jattn_plan_info", "jattn_plan_export", "jattn_plan_upload",
                  "jattn_fwd", "jattn_bwd", "jattn_bwd_stages", "jattn_bwd_fixed_scratch", "jattn_l2norm_fwd",
-                 "jattn_l2norm_bwd"]:
+                 "jattn_l2norm_bwd", "jattn_mx_sizes", "jattn_mx_quantize", "jattn_mx_fwd", "jattn_mx_bwd"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -149,6 +160,28 @@ def jattn_bwd_stages(plan, stages, q, k, v, bias, o, lse, dout, dq, dk, dv, dbia
 
 def jattn_bwd_fixed_scratch(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream) -> None:
     _check(lib().jattn_bwd_fixed_scratch(plan, q, k, v, bias, o, lse, dout, dq, dk, dv, dbias, workspace, stream))
+
+
+def jattn_mx_sizes(plan, rows):
+    """(codes, codes_t, scales) byte sizes of an MXFP8 tensor of the plan."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().jattn_mx_sizes(plan, rows, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def jattn_mx_quantize(plan, rows, x, out: jattn_mx_tensor, workspace, stream) -> None:
+    _check(lib().jattn_mx_quantize(plan, rows, x, ctypes.byref(out), workspace, stream))
+
+
+def jattn_mx_fwd(plan, q: jattn_mx_tensor, k: jattn_mx_tensor, v: jattn_mx_tensor, o, lse, workspace,
+                 stream) -> None:
+    _check(lib().jattn_mx_fwd(plan, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), o, lse, workspace, stream))
+
+
+def jattn_mx_bwd(plan, stages, q: jattn_mx_tensor, k: jattn_mx_tensor, v: jattn_mx_tensor, o, lse,
+                 dout: jattn_mx_tensor, dq, dk, dv, workspace, stream) -> None:
+    _check(lib().jattn_mx_bwd(plan, stages, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), o, lse,
+                              ctypes.byref(dout), dq, dk, dv, workspace, stream))
 
 
 def jattn_l2norm_fwd(x, y, rnorm, rows, D, x_dtype, y_dtype, stream) -> None:

@@ -46,6 +46,8 @@ def units():
             u.append(("dq2_inst.hip", f"dq2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
         u.append(("bwd_inst.hip", f"di_{d}_bf16", [f"-DJ_D={d}", "-DJ_TI=bf16", "-DJ_TG=bf16", "-DJ_DI",
                                                    "-DJ_DI_ONLY"]))
+    for d in (128, 64):
+        u.append(("mx_inst.hip", f"mx_{d}", [f"-DJ_D={d}"]))
     for d in F32_DIMS:
         u.append(("fwd_inst.hip", f"fwd_{d}_f32_f32", [f"-DJ_D={d}", "-DJ_TI=f32", "-DJ_TO=f32"]))
         u.append(("bwd_inst.hip", f"bwd_{d}_f32_f32", [f"-DJ_D={d}", "-DJ_TI=f32", "-DJ_TG=f32", "-DJ_DI"]))
@@ -71,15 +73,40 @@ def _scratch_kernels(text):
     return bad
 
 
+def _dep_files(depfile):
+    """Files a translation unit depends on, from the compiler's make-style
+    dependency output (None if it is missing)."""
+    try:
+        text = open(depfile).read().replace("\\\n", " ")
+    except OSError:
+        return None
+    deps = []
+    for line in text.splitlines():
+        if ":" in line:
+            deps += line.split(":", 1)[1].split()
+    return deps
+
+
+def _up_to_date(out, depfile):
+    if not os.path.exists(out):
+        return False
+    deps = _dep_files(depfile)
+    if not deps:
+        deps = _deps()
+    try:
+        return os.path.getmtime(out) >= max(os.path.getmtime(p) for p in deps + [__file__])
+    except OSError:
+        return False
+
+
 def _compile(src, name, defs, incremental):
     out = os.path.join(OBJ, name + ".o")
-    if incremental and os.path.exists(out):
-        newest = max(os.path.getmtime(p) for p in _deps())
-        if os.path.getmtime(out) >= newest:
-            return out, None
+    depfile = os.path.join(OBJ, name + ".d")
+    if incremental and _up_to_date(out, depfile):
+        return out, None
     hip = src.endswith(".hip")
     xflags = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if hip else []
-    cmd = [HIPCC] + FLAGS + defs + xflags + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + defs + xflags + ["-MD", "-MF", depfile, "-c", os.path.join(CSRC, src), "-o", out]
     p = subprocess.run(cmd, capture_output=True, text=True)
     text = p.stdout + p.stderr
     errs = "\n".join(l for l in text.splitlines()

@@ -29,6 +29,9 @@ struct jattn_plan {
   int64_t off_samples = 0, off_fwd_u = 0, off_fwd_o = 0, off_dkdv_u = 0, off_dkdv_o = 0;
   int64_t off_dq_u = 0, off_dq_o = 0, off_blk_u = 0, off_blk_o = 0;  // in int32 words
   int64_t off_theta = -1;  // RoPE theta table (fp64), in int32 words; -1 without RoPE
+  // MXFP8: 32-row block tables (first row, rows) of the query and key rows
+  bool mx = false;
+  int64_t rb_q = 0, rb_k = 0, off_qblk = -1, off_kblk = -1;
   int64_t plan_bytes = 0, di_off = 0, lse2_off = 0, workspace_bytes = 0;
 };
 
@@ -130,7 +133,14 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     if (d.want_dbias)
       return fail(JATTN_E_UNSUPPORTED, "sliding-window mode does not produce dbias (dense [H, lq, lk] layout)");
   }
-  if (d.in_dtype != JATTN_BF16 && d.in_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown in_dtype");
+  if (d.in_dtype != JATTN_BF16 && d.in_dtype != JATTN_F32 && d.in_dtype != JATTN_MXFP8)
+    return fail(JATTN_E_UNSUPPORTED, "unknown in_dtype");
+  if (d.in_dtype == JATTN_MXFP8) {
+    if (d.D != 64 && d.D != 128) return fail(JATTN_E_UNSUPPORTED, "MXFP8 attention supports D = 64 or 128");
+    if (d.mask != JATTN_MASK_NONE) return fail(JATTN_E_UNSUPPORTED, "MXFP8 attention has no block or window mask");
+    if (d.has_bias) return fail(JATTN_E_UNSUPPORTED, "MXFP8 attention takes no bias");
+    if (d.act == JATTN_GELU_POLY) return fail(JATTN_E_UNSUPPORTED, "MXFP8 attention: softmax, erf-GELU or SiLU");
+  }
   if (d.out_dtype != JATTN_BF16 && d.out_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown out_dtype");
   if (d.grad_dtype != JATTN_BF16 && d.grad_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown grad_dtype");
   if (d.dbias_dtype != JATTN_BF16 && d.dbias_dtype != JATTN_F32) return fail(JATTN_E_UNSUPPORTED, "unknown dbias_dtype");
@@ -208,6 +218,14 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     s[3] = lk[b];
     s[4] = (int32_t)(uint32_t)(bias0 & 0xffffffffLL);
     s[5] = (int32_t)(bias0 >> 32);
+    if (d.in_dtype == JATTN_MXFP8) {
+      // first 32-row block of the sample's queries / keys (MXFP8 scale and
+      // transposed-code row blocks)
+      s[6] = (int32_t)p->rb_q;
+      s[7] = (int32_t)p->rb_k;
+      p->rb_q += (lq[b] + 31) / 32;
+      p->rb_k += (lk[b] + 31) / 32;
+    }
     bias0 += (int64_t)d.H * lq[b] * lk[b];
     if (d.mask == JATTN_MASK_BLOCKDIAG64) {
       for (int s0 = 0; s0 < lq[b]; s0 += 64) {
@@ -234,6 +252,14 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   const jattn::Order order = (jattn::Order)d.order;
   if (d.mask == JATTN_MASK_BLOCKDIAG64) {
     jattn::plan_units(jattn::kKindBlock, lq, lk, d.H, 64, 64, W, order, &p->block);
+  } else if (d.in_dtype == JATTN_MXFP8) {
+    // MXFP8 forward: 128-row query tiles (four waves of 32 rows), 64-key steps
+    p->mx = true;
+    p->fwd_wq = 4;
+    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, 128, 64, W, order, &p->fwd);
+    // backward: dK/dV over 128-key tiles with 64-query steps, dQ like the forward
+    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, 128, 64, W, order, &p->dkdv);
+    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, 128, 64, W, order, &p->dq);
   } else {
     // Query-tile shape: 4 waves x 32 rows, or (short queries) one 32-row
     // group whose key tiles are split over the 4 waves.
@@ -285,6 +311,20 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
       p->image.push_back(w[0]);
       p->image.push_back(w[1]);
     }
+  }
+  if (p->mx) {
+    // 32-row block tables of the quantiser: (first row, rows) per block
+    auto blocks = [&](const int64_t* off, int64_t* at) {
+      p->image.resize((size_t)align_up((int64_t)p->image.size(), 4), 0);
+      *at = (int64_t)p->image.size();
+      for (int b = 0; b < B; ++b)
+        for (int64_t r = off[b]; r < off[b + 1]; r += 32) {
+          p->image.push_back((int32_t)r);
+          p->image.push_back((int32_t)std::min<int64_t>(32, off[b + 1] - r));
+        }
+    };
+    blocks(q_offsets, &p->off_qblk);
+    blocks(kv_offsets, &p->off_kblk);
   }
   p->plan_bytes = (int64_t)p->image.size() * 4;
   p->di_off = align_up(p->plan_bytes, 256);
@@ -353,6 +393,7 @@ int jattn_plan_upload(const jattn_plan* p, void* workspace, int64_t workspace_by
 int jattn_fwd(const jattn_plan* p, const void* q, const void* k, const void* v, const void* bias, void* o,
               float* lse, void* workspace, void* stream) {
   if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (p->mx) return fail(JATTN_E_UNSUPPORTED, "an MXFP8 plan runs through jattn_mx_fwd");
   if (p->Tq == 0) return ok();
   if (!q || !o || (p->Tk > 0 && (!k || !v))) return fail(JATTN_E_NULL, "null q/k/v/o");
   if (p->desc.has_bias && !bias && p->bias_elems > 0) return fail(JATTN_E_NULL, "bias required (has_bias = 1)");
@@ -431,6 +472,7 @@ int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, c
             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias,
             void* workspace, void* stream, bool fixed_scratch) {
   if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (p->mx) return fail(JATTN_E_UNSUPPORTED, "an MXFP8 plan has no bf16 backward");
   if (stages < 0 || stages > JATTN_BWD_ALL) return fail(JATTN_E_ARG, "unknown backward stage mask");
   // softmax outside block mode keeps row statistics from the forward
   const bool softmax_dense = p->desc.act == JATTN_SOFTMAX && p->desc.mask != JATTN_MASK_BLOCKDIAG64;
@@ -546,6 +588,162 @@ int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, c
 extern "C" {
 
 void jattn_plan_destroy(jattn_plan* p) { delete p; }
+
+int jattn_mx_sizes(const jattn_plan* p, int32_t rows, int64_t* codes_bytes, int64_t* codes_t_bytes,
+                   int64_t* scales_bytes) {
+  if (!p || !codes_bytes || !codes_t_bytes || !scales_bytes) return fail(JATTN_E_NULL, "null argument");
+  if (!p->mx) return fail(JATTN_E_UNSUPPORTED, "not an MXFP8 plan");
+  if (rows != JATTN_MX_Q && rows != JATTN_MX_KV) return fail(JATTN_E_ARG, "rows must be JATTN_MX_Q or JATTN_MX_KV");
+  const int64_t T = rows == JATTN_MX_Q ? p->Tq : p->Tk;
+  const int64_t RB = rows == JATTN_MX_Q ? p->rb_q : p->rb_k;
+  *codes_bytes = T * p->H * p->D;
+  *codes_t_bytes = RB * p->H * p->D * 32;
+  // rounded up to whole dwords: the kernels read scale bytes as aligned dwords
+  *scales_bytes = align_up(RB * p->H * (p->D / 32), 4);
+  return ok();
+}
+
+int jattn_mx_quantize(const jattn_plan* p, int32_t rows, const void* x, const jattn_mx_tensor* out, void* workspace,
+                      void* stream) {
+  if (!p || !out) return fail(JATTN_E_NULL, "null plan or output");
+  if (!p->mx) return fail(JATTN_E_UNSUPPORTED, "not an MXFP8 plan");
+  if (rows != JATTN_MX_Q && rows != JATTN_MX_KV) return fail(JATTN_E_ARG, "rows must be JATTN_MX_Q or JATTN_MX_KV");
+  const int64_t T = rows == JATTN_MX_Q ? p->Tq : p->Tk;
+  const int64_t RB = rows == JATTN_MX_Q ? p->rb_q : p->rb_k;
+  if (T == 0) return ok();
+  if (!x || !out->codes || !out->scales) return fail(JATTN_E_NULL, "null x / codes / scales");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(x, 16) || !aligned(out->codes, 16) || (out->codes_t && !aligned(out->codes_t, 16)))
+    return fail(JATTN_E_ALIGN, "x / codes / codes_t must be 16-byte aligned");
+  jattn::MxQuantArgs a{};
+  a.x = x;
+  a.codes = static_cast<uint8_t*>(out->codes);
+  a.codes_t = static_cast<uint8_t*>(out->codes_t);
+  a.scales = static_cast<uint8_t*>(out->scales);
+  a.blocks = ws_ptr(workspace, rows == JATTN_MX_Q ? p->off_qblk : p->off_kblk);
+  a.H = p->H;
+  a.nblocks = RB;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = p->D == 128 ? jattn::launch_mx_quant_128(a, st) : jattn::launch_mx_quant_64(a, st);
+  if (e != hipSuccess) return hip_fail(e, "MXFP8 quantisation launch");
+  return ok();
+}
+
+int jattn_mx_bwd(const jattn_plan* p, int32_t stages, const jattn_mx_tensor* q, const jattn_mx_tensor* k,
+                 const jattn_mx_tensor* v, const void* o, const float* lse, const jattn_mx_tensor* dout, void* dq,
+                 void* dk, void* dv, void* workspace, void* stream) {
+  if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (!p->mx) return fail(JATTN_E_UNSUPPORTED, "not an MXFP8 plan");
+  if (stages < 0 || stages > JATTN_BWD_ALL) return fail(JATTN_E_ARG, "unknown backward stage mask");
+  if (p->Tq == 0 && p->Tk == 0) return ok();
+  const bool softmax = p->desc.act == JATTN_SOFTMAX;
+  if (!q || !k || !v || !dout) return fail(JATTN_E_NULL, "null q / k / v / dout");
+  if ((p->Tq > 0 && (!q->codes || !q->codes_t || !q->scales || !dout->codes || !dout->codes_t || !dout->scales ||
+                     !dq)) ||
+      (p->Tk > 0 && (!k->codes || !k->codes_t || !k->scales || !v->codes || !v->scales || !dk || !dv)))
+    return fail(JATTN_E_NULL, "the backward reads q, dout (codes, codes_t, scales), k (codes, codes_t, scales), "
+                              "v (codes, scales) and writes dq, dk, dv");
+  if (softmax && p->Tq > 0 && (!o || !lse)) return fail(JATTN_E_STATE, "softmax backward needs o and lse");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  for (const jattn_mx_tensor* t : {q, k, v, dout})
+    if ((t->codes && !aligned(t->codes, 16)) || (t->codes_t && !aligned(t->codes_t, 16)) ||
+        (t->scales && !aligned(t->scales, 4)))
+      return fail(JATTN_E_ALIGN, "codes / codes_t must be 16-byte aligned, scales 4-byte aligned");
+  if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || (o && !aligned(o, 16)) || (lse && !aligned(lse, 4)))
+    return fail(JATTN_E_ALIGN, "o / dq / dk / dv must be 16-byte aligned, lse 4-byte aligned");
+  auto tens = [](const jattn_mx_tensor* t) {
+    return jattn::MxTensor{static_cast<const uint8_t*>(t->codes), static_cast<const uint8_t*>(t->codes_t),
+                           static_cast<const uint8_t*>(t->scales)};
+  };
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* di = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->di_off);
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->lse2_off);
+  hipError_t e;
+  if (softmax && p->Tq > 0 && (stages & JATTN_BWD_PREP)) {
+    jattn::MxDiArgs da{};
+    da.dout = tens(dout);
+    da.o = o;
+    da.lse = lse;
+    da.di = di;
+    da.lse2 = lse2;
+    da.blocks = ws_ptr(workspace, p->off_qblk);
+    da.H = p->H;
+    da.nblocks = p->rb_q;
+    const bool of32 = p->desc.out_dtype == JATTN_F32;
+    e = p->D == 128 ? jattn::launch_mx_di_128(da, of32, st) : jattn::launch_mx_di_64(da, of32, st);
+    if (e != hipSuccess) return hip_fail(e, "MXFP8 Di launch");
+  }
+  jattn::MxBwdArgs a{};
+  a.q = tens(q);
+  a.k = tens(k);
+  a.v = tens(v);
+  a.dout = tens(dout);
+  a.di = di;
+  a.lse2 = lse2;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.samples = ws_ptr(workspace, p->off_samples);
+  a.H = p->H;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.4426950408889634f;
+  const bool gf32 = p->desc.grad_dtype == JATTN_F32;
+  if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
+    a.units = ws_ptr(workspace, p->off_dkdv_u);
+    a.worker_off = ws_ptr(workspace, p->off_dkdv_o);
+    e = p->D == 128 ? jattn::launch_mx_dkdv_128(a, p->desc.act, gf32, p->dkdv.num_workers, st)
+                    : jattn::launch_mx_dkdv_64(a, p->desc.act, gf32, p->dkdv.num_workers, st);
+    if (e != hipSuccess) return hip_fail(e, "MXFP8 dK/dV launch");
+  }
+  if (p->dq.n_units() > 0 && (stages & JATTN_BWD_DQ)) {
+    a.units = ws_ptr(workspace, p->off_dq_u);
+    a.worker_off = ws_ptr(workspace, p->off_dq_o);
+    e = p->D == 128 ? jattn::launch_mx_dq_128(a, p->desc.act, gf32, p->dq.num_workers, st)
+                    : jattn::launch_mx_dq_64(a, p->desc.act, gf32, p->dq.num_workers, st);
+    if (e != hipSuccess) return hip_fail(e, "MXFP8 dQ launch");
+  }
+  return ok();
+}
+
+int jattn_mx_fwd(const jattn_plan* p, const jattn_mx_tensor* q, const jattn_mx_tensor* k, const jattn_mx_tensor* v,
+                 void* o, float* lse, void* workspace, void* stream) {
+  if (!p) return fail(JATTN_E_NULL, "null plan");
+  if (!p->mx) return fail(JATTN_E_UNSUPPORTED, "not an MXFP8 plan");
+  if (p->Tq == 0) return ok();
+  if (!q || !k || !v || !o) return fail(JATTN_E_NULL, "null q / k / v / o");
+  if (!q->codes || !q->scales || (p->Tk > 0 && (!k->codes || !k->scales || !v->codes_t || !v->scales)))
+    return fail(JATTN_E_NULL, "the forward reads q and k codes, v transposed codes and all three scales");
+  if (!workspace) return fail(JATTN_E_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(JATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(q->codes, 16) || (p->Tk > 0 && (!aligned(k->codes, 16) || !aligned(v->codes_t, 16))) ||
+      !aligned(o, 16) || !aligned(q->scales, 4) || (p->Tk > 0 && (!aligned(k->scales, 4) || !aligned(v->scales, 4))))
+    return fail(JATTN_E_ALIGN, "codes and o must be 16-byte aligned, scales 4-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(JATTN_E_ALIGN, "lse must be 4-byte aligned");
+  jattn::MxFwdArgs a{};
+  auto tens = [](const jattn_mx_tensor* t) {
+    return jattn::MxTensor{static_cast<const uint8_t*>(t->codes), static_cast<const uint8_t*>(t->codes_t),
+                           static_cast<const uint8_t*>(t->scales)};
+  };
+  a.q = tens(q);
+  a.k = tens(k);
+  a.v = tens(v);
+  a.o = o;
+  a.lse = p->desc.act == JATTN_SOFTMAX ? lse : nullptr;
+  a.units = ws_ptr(workspace, p->off_fwd_u);
+  a.worker_off = ws_ptr(workspace, p->off_fwd_o);
+  a.samples = ws_ptr(workspace, p->off_samples);
+  a.H = p->H;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * 1.4426950408889634f;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool of32 = p->desc.out_dtype == JATTN_F32;
+  const hipError_t e = p->D == 128 ? jattn::launch_mx_fwd_128(a, p->desc.act, of32, p->fwd.num_workers, st)
+                                   : jattn::launch_mx_fwd_64(a, p->desc.act, of32, p->fwd.num_workers, st);
+  if (e != hipSuccess) return hip_fail(e, "MXFP8 forward launch");
+  return ok();
+}
 
 namespace {
 int l2norm_check(int64_t rows, int32_t D, std::initializer_list<int32_t> dtypes) {

@@ -64,6 +64,61 @@ struct BwdArgs {
   const double* rope_theta;  // block mode with RoPE: theta_j, j < D/2 (else null)
 };
 
+// MXFP8 tensor as the kernels see it (see mx_impl.hpp for the layout)
+struct MxTensor {
+  const uint8_t* codes;    // [T, H, D] E4M3 codes
+  const uint8_t* codes_t;  // [RB, H, D, 32] the same, per 32-token block, feature-major
+  const uint8_t* scales;   // [RB, H, D/32] E8M0 bytes
+};
+
+struct MxQuantArgs {
+  const void* x;           // bf16 [T, H, D]
+  uint8_t* codes;
+  uint8_t* codes_t;        // may be null (not written)
+  uint8_t* scales;
+  const int32_t* blocks;   // [RB][2]: first row, rows of each 32-row block
+  int H;
+  int64_t nblocks;
+};
+
+struct MxFwdArgs {
+  MxTensor q, k, v;
+  void* o;
+  float* lse;
+  const int32_t* units;
+  const int32_t* worker_off;
+  const int32_t* samples;  // entries 6, 7: first row block of the sample's queries / keys
+  int H;
+  float scale;
+  float scale_log2;
+};
+
+struct MxDiArgs {
+  MxTensor dout;           // codes, scales of dO
+  const void* o;           // out dtype [Tq, H, D]
+  const float* lse;        // [Tq, H]
+  float* di;               // out [Tq, H]
+  float* lse2;             // out [Tq, H]: lse * log2(e)
+  const int32_t* blocks;   // [RBq][2] query row blocks
+  int H;
+  int64_t nblocks;
+};
+
+struct MxBwdArgs {
+  MxTensor q, k, v, dout;
+  const float* di;         // [Tq, H]
+  const float* lse2;       // [Tq, H]
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* units;
+  const int32_t* worker_off;
+  const int32_t* samples;
+  int H;
+  float scale;
+  float scale_log2;
+};
+
 // Which template instance to run.
 struct KernelSel {
   int D;          // 32, 64, 128
@@ -136,6 +191,18 @@ hipError_t launch_di(const DiArgs& a, const KernelSel& k, bool o_f32, hipStream_
 // workers (wave pairs) of the block plan.
 hipError_t launch_block_fwd(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
 hipError_t launch_block_bwd(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st);
+
+// MXFP8 (mx_inst.hip, one translation unit per head dim)
+hipError_t launch_mx_quant_128(const MxQuantArgs&, hipStream_t);
+hipError_t launch_mx_quant_64(const MxQuantArgs&, hipStream_t);
+hipError_t launch_mx_fwd_128(const MxFwdArgs&, int act, bool out_f32, int grid, hipStream_t);
+hipError_t launch_mx_fwd_64(const MxFwdArgs&, int act, bool out_f32, int grid, hipStream_t);
+hipError_t launch_mx_di_128(const MxDiArgs&, bool o_f32, hipStream_t);
+hipError_t launch_mx_di_64(const MxDiArgs&, bool o_f32, hipStream_t);
+hipError_t launch_mx_dkdv_128(const MxBwdArgs&, int act, bool grad_f32, int grid, hipStream_t);
+hipError_t launch_mx_dkdv_64(const MxBwdArgs&, int act, bool grad_f32, int grid, hipStream_t);
+hipError_t launch_mx_dq_128(const MxBwdArgs&, int act, bool grad_f32, int grid, hipStream_t);
+hipError_t launch_mx_dq_64(const MxBwdArgs&, int act, bool grad_f32, int grid, hipStream_t);
 
 // Fixed device scratch (fixed_scratch.hip): its size, and its address on the
 // current device (looked up on the first call per device, then kept).

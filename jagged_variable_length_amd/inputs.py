@@ -52,6 +52,7 @@ class Workload:
     scale: Optional[float] = None  # score scale; None = 1/sqrt(D)
     rope: bool = False  # block mode: rotary embedding of Q and K fused into the kernels
     seed: Optional[int] = None  # canonical seed; None = the workload index
+    mxfp8: bool = False  # inputs quantised to MXFP8 (32 x 32 blocks) and MXFP8 products
 
 
 WORKLOADS = {
@@ -74,6 +75,10 @@ WORKLOADS = {
     # bound by the bias stream
     8: Workload("jfa_self_nobias", 256, 4, 128, "bf16", ACT_SOFTMAX, False, False, False, "bf16", "bf16", False,
                 seed=1),
+    # workload 8 in MXFP8: Q, K, V, dO quantised in 32 x 32 blocks, MXFP8
+    # products forward and backward, fp32 outputs and gradients
+    9: Workload("jfa_self_mxfp8", 256, 4, 128, "bf16", ACT_SOFTMAX, False, False, False, "f32", "f32", False,
+                seed=1, mxfp8=True),
 }
 
 
@@ -119,7 +124,7 @@ def _lengths_from(rng, cfg):
         lq = rng.integers(1, 65, w.B).astype(np.int64)
         lq[1] = 0  # one zero-length sample
         return lq, lq.copy()
-    if cfg in (1, 8):
+    if cfg in (1, 8, 9):
         lq = _lognormal_lengths(rng, w.B, 300, 8, 1000)
         return lq, lq.copy()
     if cfg == 2:
