@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="write profiles/mfma.json for --config from a rocprofv3 MFMA counter run in DIR")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CALIB_FETCH", "CALIB_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE of this workload; "
                          "the same two of --copy-calib) into profiles/traffic.json and exit")
@@ -115,7 +117,7 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-KERNEL_KEYS = [("block_fwd_kernel", "block_fwd"), ("block_bwd_kernel", "block_bwd"), ("dkdv", "dkdv"),
+KERNEL_KEYS = [("mx_quant_kernel", "quant"), ("block_fwd_kernel", "block_fwd"), ("block_bwd_kernel", "block_bwd"), ("dkdv", "dkdv"),
                ("dq2_kernel", "dq"), ("dq_kernel", "dq"), ("fwd2_kernel", "fwd"), ("fwd_kernel", "fwd"),
                ("di_kernel", "prep"), ("l2norm_fwd_kernel", "qknorm"), ("l2norm_bwd_kernel", "qknorm_bwd")]
 
@@ -199,6 +201,77 @@ def traffic_summary(args):
     with open(p, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def _pmc_rows(folder):
+    """Rows of the *counter_collection.csv files rocprofv3 wrote under `folder`."""
+    import csv
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    yield from csv.DictReader(fh)
+
+
+def mfma_summary(args):
+    """MFMA utilisation and shader clock of each attention kernel from one
+    rocprofv3 run with --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8.
+
+    MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max over XCDs of
+    GRBM_GUI_ACTIVE * 1024 SIMDs), rocprofiler's own definition; the csv
+    carries GRBM_GUI_ACTIVE summed over the XCDs, so the per-XCD maximum is
+    recovered from that definition, and the clock is that many cycles over the
+    dispatch's duration (a lower bound: the duration includes launch edges).
+    MOPS counters give the MFMA work actually executed (x 512 FLOP)."""
+    per = {}
+    for row in _pmc_rows(args.mfma_summary):
+        key = (row["Kernel_Name"], row["Dispatch_Id"])
+        d = per.setdefault(key, {"ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+        d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    by = {}
+    for (name, _), d in per.items():
+        by.setdefault(name, []).append(d)
+    res = {}
+    for name, ds in by.items():
+        key = kernel_key(name)
+        if key is None:
+            continue
+        m = lambda c: float(np.mean([d.get(c, 0.0) for d in ds]))
+        util, busy, ns = m("MfmaUtil"), m("SQ_VALU_MFMA_BUSY_CYCLES"), m("ns")
+        gui_max = busy * 100.0 / (util * 1024) if util > 0 else None
+        res[key] = {"kernel": name, "dispatches": len(ds), "mfma_util_pct": round(util, 2),
+                    "mfma_busy_cycles": busy, "grbm_gui_active_sum": m("GRBM_GUI_ACTIVE"),
+                    "grbm_gui_active_max_xcd": gui_max, "duration_us": round(ns / 1e3, 2),
+                    "clock_mhz": round(gui_max / ns * 1e3, 0) if gui_max else None,
+                    "mfma_flops_bf16": m("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512,
+                    "mfma_flops_f8": m("SQ_INSTS_VALU_MFMA_MOPS_F8") * 512}
+    out = {"source_hash": source_hash(), "workloads": {str(args.config): res}}
+    p = os.path.join(ROOT, "profiles", "mfma.json")
+    if os.path.exists(p):
+        try:
+            old = json.load(open(p))
+        except (OSError, ValueError):
+            old = {}
+        if old.get("source_hash") == out["source_hash"]:
+            old.get("workloads", {}).update(out["workloads"])
+            out["workloads"] = old["workloads"]
+    with open(p, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def mfma_for(kernel, cfg):
+    """Counter record of `kernel` on workload `cfg` (profiles/mfma.json), if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "mfma.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("workloads", {}).get(str(cfg), {}).get(kernel)
 
 
 def _window_pairs(n, window):
@@ -423,6 +496,9 @@ def main():
     if args.traffic_summary:
         traffic_summary(args)
         return
+    if args.mfma_summary:
+        mfma_summary(args)
+        return
 
     import torch
     from jagged_variable_length_amd import attention as A
@@ -569,10 +645,20 @@ def main():
                       "ms_min": round(float(np.min(times[n])), 4), "GB/s": round(b_ / (ms[n] * 1e-3) / 1e9, 1),
                       "TFLOP/s": round(f_ / (ms[n] * 1e-3) / 1e12, 2)}
 
+    # MFMA counters of the dominant kernel, when profiles/mfma.json was taken
+    # on these kernel sources: utilisation and the clock it ran at
+    mf = mfma_for(dom, cfg)
+    clock_info = None
+    if mf:
+        roof["mfma_util_pct"] = mf["mfma_util_pct"]
+        clock_info = {"mhz": mf["clock_mhz"], "kernel": dom, "source": "GRBM_GUI_ACTIVE per XCD / dispatch duration "
+                      "(rocprofv3 counters, profiles/mfma.json)"}
+        # the dense MFMA peak at that clock: 1024 SIMDs x 1024 FLOP/clk (bf16), 2048 (fp8)
+        per_clk = 2048 if w.mxfp8 else (256 if w.dtype == "f32" else 1024)
+        roof["mfma_peak_at_clock_tflops"] = round(1024 * per_clk * mf["clock_mhz"] * 1e6 / 1e12, 1)
     clk = clock.summary()
     if clk:
-        # the dense bf16 MFMA peak at the sampled clock: 256 CU x 4096 FLOP/clk
-        roof["peak_at_sampled_clock_tflops"] = round(256 * 4096 * clk["sclk_mhz_median"] * 1e6 / 1e12, 1)
+        clock_info = dict(clock_info or {}, sysfs_sclk=clk)
     out = {
         "metric": "jagged attn fwd+bwd TFLOPs (valid tokens) and % of bf16 MFMA peak, 1 GPU",
         "value": round(value, 3),
@@ -601,7 +687,7 @@ def main():
                    "dbias_dtype": w.dbias_dtype if w.want_dbias else None},
         "kernels": kernels,
         "roofline": roof,
-        "clock": clock.summary(),
+        "clock": clock_info,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
