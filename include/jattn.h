@@ -71,7 +71,8 @@ extern "C" {
 #define JATTN_OK 0
 #define JATTN_E_NULL (-1)        /* a required pointer is NULL */
 #define JATTN_E_OFFSETS (-2)     /* offsets[0] != 0, decreasing, or a total >= 2^31 rows */
-#define JATTN_E_SHAPE (-3)       /* bad B, H, D, or block-diagonal with lq != lk */
+#define JATTN_E_SHAPE (-3)       /* bad B, H, D, block-diagonal with lq != lk, or a sample whose rows span
+                                    >= 2^31 bytes in the widest of in/out/grad dtype */
 #define JATTN_E_UNSUPPORTED (-4) /* unsupported dtype / activation / mask combination */
 #define JATTN_E_ALIGN (-5)       /* misaligned device pointer */
 #define JATTN_E_WORKSPACE (-6)   /* workspace missing or too small */

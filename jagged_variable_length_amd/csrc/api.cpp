@@ -169,7 +169,10 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
   if (q_offsets[0] != 0 || kv_offsets[0] != 0) return fail(JATTN_E_OFFSETS, "offsets[0] must be 0");
   std::vector<int32_t> lq(B), lk(B);
   const int es = elem_size(d.in_dtype);
-  const int64_t row_bytes = (int64_t)d.H * d.D * es;
+  // kernels address one sample's rows of any input, output or gradient with
+  // 32-bit byte offsets, and mark lanes without a row by offsets >= 2^31
+  const int es_max = std::max(es, std::max(elem_size(d.out_dtype), elem_size(d.grad_dtype)));
+  const int64_t row_bytes = (int64_t)d.H * d.D * es_max;
   for (int b = 0; b < B; ++b) {
     const int64_t a = q_offsets[b + 1] - q_offsets[b];
     const int64_t c = kv_offsets[b + 1] - kv_offsets[b];

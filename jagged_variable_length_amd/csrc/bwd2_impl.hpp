@@ -44,37 +44,9 @@
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
+#include "ring.hpp"
 
 namespace jattn {
-
-// Plan records through scalar loads: addresses are wave-uniform and the data
-// is read-only for the whole launch, so the constant address space applies.
-// Scalar loads are counted by lgkmcnt, which keeps the compiler from placing
-// vmcnt waits (and with them waits on the LDS prefetches) on plan reads.
-typedef __attribute__((address_space(4))) const int32_t c_i32;
-typedef __attribute__((address_space(4))) const i32x4 c_i32x4;
-
-__device__ __forceinline__ int sload1(const int32_t* p, int i) { return ((c_i32*)p)[i]; }
-__device__ __forceinline__ i32x4 sload4(const int32_t* p, int i) { return ((c_i32x4*)p)[i]; }
-
-__device__ __forceinline__ Sample sload_sample(const int32_t* table, int b) {
-  const i32x4 x = sload4(table, 2 * b);
-  const i32x4 y = sload4(table, 2 * b + 1);
-  Sample s;
-  s.q0 = x[0];
-  s.lq = x[1];
-  s.k0 = x[2];
-  s.lk = x[3];
-  s.bias0 = (int64_t)(uint32_t)y[0] | ((int64_t)y[1] << 32);
-  return s;
-}
-
-// s_waitcnt vmcnt(n), n <= 63 (expcnt and lgkmcnt at their maximum)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 
 template <int D, int WKV, int WKQ, bool SOFTMAX, bool BIAS>
 struct Dkdv2Shape {
@@ -105,26 +77,6 @@ struct Dkdv2Shape {
   static_assert(NS_FIT >= 3 && COMB <= STAGE, "LDS budget");
   static_assert(NW == 4, "four waves");
 };
-
-// Number of the NI load instructions part, part + NP, ... that wave `part` issues.
-__device__ __forceinline__ constexpr int loads_of(int NI, int part, int NP) {
-  return part < NI ? (NI - part + NP - 1) / NP : 0;
-}
-
-// s_waitcnt vmcnt(n) for a runtime n (clamped to 0..63): binary dispatch to
-// compile-time immediates.
-template <int LO, int HI>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if constexpr (LO == HI) {
-    wait_vmcnt<LO>();
-  } else {
-    constexpr int MID = (LO + HI + 1) / 2;
-    if (n >= MID)
-      wait_vmcnt_le<MID, HI>(n);
-    else
-      wait_vmcnt_le<LO, MID - 1>(n);
-  }
-}
 
 // DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
 template <typename TG, int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT, bool WIN = false>

@@ -14,8 +14,11 @@
 //     dS^T = P^T (dP^T - Di)              (or act'(S^T*scale + bias) dP^T)
 //     dQ^T += K^T dS^T A = K^T via ds_read_b64_tr_b16, B = dS^T in-register
 // K, V and the bias tile travel HBM -> LDS with buffer loads whose
-// destination is LDS, double-buffered across steps and units; the key-split
-// partials of dQ are summed through LDS at the end of a unit.  K and V rows
+// destination is LDS into a ring of NS stages: a producer cursor runs NS - 1
+// steps ahead of the step being computed, across unit boundaries, and each
+// step waits only for its own loads (exact per-wave counts, dQ stores
+// included).  The key-split partials of dQ are summed through LDS at the end
+// of a unit.  K and V rows
 // are stored permuted within each 32-key block (RowLoader PERM), so that the
 // 16 scores of a lane are 16 consecutive keys and its bias values are two
 // aligned 16-byte LDS reads.
@@ -24,10 +27,13 @@
 // the first key tile its window meets; dS is zeroed element-wise in 32x32
 // blocks that are not wholly inside the window.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
+#include "ring.hpp"
 
 namespace jattn {
 
@@ -45,23 +51,31 @@ struct Dq2Shape {
   using BT = PadTile<BN, 1>;  // bias rows: pitch = 16 (mod 256) bytes, 16-byte reads conflict-free
   static constexpr int B_BYTES = BIAS ? BT::template bytes<BM>() : 0;
   static constexpr int STAGE = K_BYTES + V_BYTES + B_BYTES;
+  // ring depth: up to four stages (three steps in flight beside the one computed)
+  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : NS_FIT;
+  static_assert(NS >= 2, "two stages at least");
+  // LDS-destination load instructions of one step (whole workgroup)
+  static constexpr int KNI = KT::template ninst<BN>();
+  static constexpr int VNI = VT::template ninst<BN>();
+  static constexpr int BNI = BIAS ? BT::template ninst<BM>() : 0;
   // dQ^T partials of key blocks 1..WK-1: one pass through a region of their
   // own when the LDS budget allows, else DP 32-column blocks of D per pass
   // through the stage of the unit's last step
   static constexpr int COMB_PER_D = (WK - 1) * WQ * 32 * 32 * 4;
   static constexpr int COMB = COMB_PER_D * ND;
-  static constexpr bool COMB_IN_STAGE = WK > 1 && 2 * STAGE + COMB > 160 * 1024;
+  static constexpr bool COMB_IN_STAGE = WK > 1 && NS * STAGE + COMB > 160 * 1024;
   static constexpr int DP_FIT = WK > 1 ? STAGE / COMB_PER_D : ND;
   static_assert(!COMB_IN_STAGE || DP_FIT >= 1, "combine pass does not fit a stage");
   static constexpr int DP = !COMB_IN_STAGE || DP_FIT >= ND ? ND : (DP_FIT >= 2 && ND % 2 == 0 ? 2 : 1);
-  static constexpr int SMEM = 2 * STAGE + (WK > 1 && !COMB_IN_STAGE ? COMB : 0);
+  static constexpr int SMEM = NS * STAGE + (WK > 1 && !COMB_IN_STAGE ? COMB : 0);
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
 template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   using Sh = Dq2Shape<D, WQ, WK, BIAS>;
-  constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW;
+  constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW, NS = Sh::NS;
   constexpr bool SOFTMAX = (ACT == kSoftmax);
 
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
@@ -69,8 +83,8 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   const int wq = wave % WQ, wk = wave / WQ;
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_begin = uniform(a.worker_off[worker]);
-  const int u_end = uniform(a.worker_off[worker + 1]);
+  const int u_begin = sload1(a.worker_off, worker);
+  const int u_end = sload1(a.worker_off, worker + 1);
   const int HD = a.H * D;
 
   auto stage_k = [&](int s) { return smem + s * Sh::STAGE; };
@@ -84,22 +98,23 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   BiasLoader<BN, 1, BM, NW> bload;
   kload.init(wave, lane, HD);
   vload.init(wave, lane, HD);
+  static_assert(decltype(kload)::NI == Sh::KNI && decltype(vload)::NI == Sh::VNI &&
+                    (!BIAS || decltype(bload)::NI == Sh::BNI),
+                "the ring's per-step counts are the loaders' instruction counts");
 
+  // Unit record: sample fields only (three are live at once: producer,
+  // current, next); descriptors are rebuilt where they are used.
   struct UnitInfo {
     int h, qt, n;
     Sample s;
-    i32x4 rk, rv;
   };
   auto fetch = [&](int u) {
     UnitInfo x;
-    const i32x4 un = load_unit(a.units, u);
+    const i32x4 un = sload4(a.units, u);
     x.h = un[1];
     x.qt = un[2];
     x.n = un[3];
-    x.s = load_sample(a.samples, un[0]);
-    const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D;
-    x.rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + kvo, 0);
-    x.rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + kvo, 0);
+    x.s = sload_sample(a.samples, un[0]);
     return x;
   };
   // First element of the unit's (sample, head) bias block.  Derived where it
@@ -110,22 +125,6 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   // key tile of step t (a windowed unit starts at its window's first tile)
   auto key_tile = [&](const UnitInfo& x, int t) {
     return WIN ? window_first_step(x.qt * BM, a.win_l, BN) + t : t;
-  };
-  auto issue_step = [&](const UnitInfo& x, int t, int st) {
-    const uint32_t sb = smem_lds + st * Sh::STAGE;
-    const int kt = key_tile(x, t);
-    const int64_t row0 = (int64_t)kt * BN;
-    const int64_t rec = (int64_t)(x.s.lk - kt * BN) * HD * 2;
-    kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
-    vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
-    if constexpr (BIAS) {
-      // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
-      if (t == 0) bload.init(wave, lane, x.s.lk);
-      const int64_t e0 = bias_elem0(x);
-      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
-      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
-      bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
-    }
   };
   // Q and dO fragments (B operands) and row statistics of this lane's query row
   auto load_q = [&](const UnitInfo& x, bf16x8* qf) {
@@ -154,13 +153,77 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   };
 
   if (u_begin >= u_end) return;
+
+  // ---- producer: the worker's steps in order, NS - 1 ahead of the consumer ----
+  // Each production moves one step's K and V rows (and bias tile) into a
+  // stage.  The descriptors start at the step's first key row and end at the
+  // sample end (rows past it read as zero); they are set up once per unit and
+  // advanced by a constant per step.
+  constexpr int LOOK = NS - 1;  // productions in flight at an acquisition
+  const int step_ops = loads_of(Sh::KNI, wave, NW) + loads_of(Sh::VNI, wave, NW) + loads_of(Sh::BNI, wave, NW);
+  constexpr int MIN_OPS = loads_of(Sh::KNI, NW - 1, NW) + loads_of(Sh::VNI, NW - 1, NW) +
+                          loads_of(Sh::BNI, NW - 1, NW);  // the wave with the fewest loads
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  constexpr int32_t KV_STEP = BN * D * 2;  // bytes of one step's rows per head (rows are H heads apart)
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Walker<false> wk_k, wk_v;  // K and V rows of the next step
+  Walker<true> wk_b;         // bias rows of the next step
+  auto start_unit = [&](const UnitInfo& x) {
+    const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D * 2;
+    const int64_t row0 = (int64_t)key_tile(x, 0) * BN;
+    const int64_t rec = ((int64_t)x.s.lk - row0) * HD * 2;
+    wk_k.start(reinterpret_cast<const char*>(a.k) + kvo, row0 * HD * 2, rec);
+    wk_v.start(reinterpret_cast<const char*>(a.v) + kvo, row0 * HD * 2, rec);
+    if constexpr (BIAS) {
+      // rows qt*BM .. of the bias block, keys from row0; the offsets follow lk
+      bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = bias_elem0(x);
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
+      wk_b.start(reinterpret_cast<const char*>(a.bias) + e0 * 2, off, (a.bias_elems - e0) * 2 - off);
+    }
+  };
+  UnitInfo pinfo = fetch(u_begin);
+  pn = pinfo.n;
+  if (pn > 0) start_unit(pinfo);
+  VmLedger<LOOK, WAIT_N> ring;
+  auto produce = [&]() {
+    if (pt >= pn && pu < u_end) {
+      // next unit with steps (units without keys have none)
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      const uint32_t sb = smem_lds + pst * Sh::STAGE;
+      kload.issue(sb, wk_k.words(), wave);
+      vload.issue(sb + Sh::K_BYTES, wk_v.words(), wave);
+      if constexpr (BIAS) bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, wk_b.words(), wave);
+      wk_k.advance(KV_STEP * a.H);
+      wk_v.advance(KV_STEP * a.H);
+      if constexpr (BIAS) wk_b.advance(BN * 2);
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
+  };
+
   UnitInfo cur = fetch(u_begin);
   bf16x8 qf[NKK], dof[NKK];
   float lse2 = 0.0f, di = 0.0f;
   load_q(cur, qf);
   load_do(cur, dof, lse2, di);
-  int stage = 0;
-  if (cur.n > 0) issue_step(cur, 0, 0);
+  // the first unit's rows have landed before anything else is issued: every
+  // later row load is followed by visible stores, so the compiler's own wait
+  // for them at a unit's first step leaves the ring in flight
+  wait_vmcnt<0>();
+  for (int j = 0; j < LOOK; ++j) produce();
+  int stage = 0;  // stage of the step computed next
 
   for (int u = u_begin; u < u_end; ++u) {
     const bool has_next = u + 1 < u_end;
@@ -174,14 +237,18 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) dqacc[d] = f32x16{};
 
-    for (int t = 0; t < n; ++t) {
-      wait_vmcnt0();
-      __syncthreads();  // step t is in LDS; every wave is done with step t-1
-      if (t + 1 < n) {
-        issue_step(cur, t + 1, stage ^ 1);
-      } else if (has_next && nxt.n > 0) {
-        issue_step(nxt, 0, stage ^ 1);
-      }
+    // LAST (step n-1) loads the next unit's rows; it is the only instance
+    // that does, so the loop over the other steps carries no register loads
+    // in flight and the compiler puts no vmcnt wait of its own into it (such
+    // a wait would count only the loads it can see and drain the whole ring).
+    auto step = [&](auto last_tag, int t) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      // step t is the oldest production in flight: wait for its loads only
+      ring.wait_oldest();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // its tiles are in LDS; every wave is done with the stage produce() refills
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
       const char* kt = stage_k(stage);
       const char* vt = stage_v(stage);
       const int kb = wk * 32;  // this wave's key block inside the step
@@ -195,7 +262,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) sacc = Elem<bf16>::mma(ka[kk], qf[kk], sacc);
       }
-      if (t + 1 == n && has_next) load_q(nxt, qf);
+      if (LAST && has_next) load_q(nxt, qf);
       {
         bf16x8 va[NKK];
 #pragma unroll
@@ -203,7 +270,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) dpacc = Elem<bf16>::mma(va[kk], dof[kk], dpacc);
       }
-      if (t + 1 == n && has_next) load_do(nxt, dof, lse2, di);
+      if (LAST && has_next) load_do(nxt, dof, lse2, di);
 
       // with a bias, slot i of this lane holds key t*BN + kb + 16g + i of
       // query row qt*BM + wq*32 + l32 (else key t*BN + kb + acc_row(i, g))
@@ -213,7 +280,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
         const char* bt = stage_b(stage) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
         bf16x8_to_f32(bt, ds);
         bf16x8_to_f32(bt + 16, ds + 8);
-        if (t + 1 == n && bias_elem0(cur) + (int64_t)cur.s.lq * cur.s.lk == a.bias_elems) {
+        if (LAST && bias_elem0(cur) + (int64_t)cur.s.lq * cur.s.lk == a.bias_elems) {
           // the tensor's last element may straddle the end of the bias range
           // by half a dword, which the range check drops: reload it
           const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(a.bias) + (a.bias_elems - 1), 2);
@@ -246,7 +313,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
           for (int i = 0; i < 16; ++i)
             ds[i] = w.allows(row0 + l32, key0 + (BIAS ? 16 * g + i : acc_row(i, g))) ? ds[i] : 0.0f;
         }
-      } else if (t + 1 == n) {
+      } else if (LAST) {
         // keys past the sample end (zero K/V rows, bias of the next row): their
         // dS must be exactly zero, whatever P overflowed to
 #pragma unroll
@@ -270,18 +337,23 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
           if constexpr (SPLIT) dqacc[d] = Elem<bf16>::mma(kf, dl, dqacc[d]);
         }
       }
-      stage ^= 1;
+      stage = stage + 1 == NS ? 0 : stage + 1;
+    };
+    if (n > 0) {
+      for (int t = 0; t + 1 < n; ++t) step(std::false_type{}, t);
+      step(std::true_type{}, n - 1);
     }
 
     // ---- epilogue: sum the key-block partials, dQ = scale * dQ^T^T ----
     const int qrow = cur.qt * BM + wq * 32 + l32;
-    TG* qrp = reinterpret_cast<TG*>(a.dq) + ((int64_t)(cur.s.q0 + qrow) * a.H + cur.h) * D;
     if constexpr (WK > 1) {
       if (n > 0) {
-        // the stage of the last step is free once every wave passes this barrier
+        // the stage of the unit's last step (the one before `stage`) is free
+        // once every wave passes this barrier: no load refills it before the
+        // next acquisition's barrier
         __syncthreads();
-        float* po = reinterpret_cast<float*>(Sh::COMB_IN_STAGE ? smem + (stage ^ 1) * Sh::STAGE
-                                                               : smem + 2 * Sh::STAGE);
+        float* po = reinterpret_cast<float*>(
+            Sh::COMB_IN_STAGE ? smem + (stage == 0 ? NS - 1 : stage - 1) * Sh::STAGE : smem + NS * Sh::STAGE);
         const int lane_off = g * 4 * 32 + l32;
 #pragma unroll
         for (int d0 = 0; d0 < ND; d0 += Sh::DP) {
@@ -307,29 +379,35 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
         }
       }
     }
-    if (wk == 0 && qrow < cur.s.lq) {
+    if (wk == 0) {
+      // buffer stores issued by every lane (rows past the sample end at an
+      // out-of-range offset), so that the count the ring's waits rely on
+      // does not depend on the data; they stay in flight across later waits
+      const rsrc_t rq = make_rsrc(reinterpret_cast<const TG*>(a.dq) + ((int64_t)cur.s.q0 * a.H + cur.h) * D,
+                                  (uint32_t)cur.s.lq * HD * (uint32_t)sizeof(TG));
+      const uint32_t vrow = qrow < cur.s.lq ? (uint32_t)(qrow * HD) * (uint32_t)sizeof(TG) : 0x80000000u;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          store4<TG>(qrp + d * 32 + i4 * 8 + g * 4, dqacc[d][i4 * 4] * a.scale, dqacc[d][i4 * 4 + 1] * a.scale,
-                     dqacc[d][i4 * 4 + 2] * a.scale, dqacc[d][i4 * 4 + 3] * a.scale);
+          buf_store4<TG>(rq, vrow + (uint32_t)(d * 32 + i4 * 8 + g * 4) * (uint32_t)sizeof(TG),
+                         dqacc[d][i4 * 4] * a.scale, dqacc[d][i4 * 4 + 1] * a.scale, dqacc[d][i4 * 4 + 2] * a.scale,
+                         dqacc[d][i4 * 4 + 3] * a.scale);
+      ring.counted(ND * 4);
     }
 
-    if (has_next) {
-      if (n == 0) {
-        // a unit without keys issued no prefetch
-        load_q(nxt, qf);
-        load_do(nxt, dof, lse2, di);
-      }
-      if (n == 0 && nxt.n > 0) {
-        wait_vmcnt0();
-        __syncthreads();
-        issue_step(nxt, 0, stage);
-      }
+    if (has_next && n == 0) {
+      // a unit without keys did not load the next unit's rows; waiting here
+      // (units without keys are rare) keeps this path from putting a wait
+      // that drains the ring into every unit's first step
+      load_q(nxt, qf);
+      load_do(nxt, dof, lse2, di);
+      wait_vmcnt<0>();
     }
     cur = nxt;
   }
+  // every production was acquired; only stores can still be in flight
+  wait_vmcnt<0>();
 }
 
 }  // namespace jattn

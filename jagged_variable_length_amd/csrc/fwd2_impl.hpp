@@ -14,9 +14,12 @@
 //     O^T += V^T P^T   A = V^T via ds_read_b64_tr_b16 from the row-major V
 //                      tile, B = P taken straight from the S^T accumulator
 // K, V and the bias tile travel HBM -> LDS with buffer loads whose
-// destination is LDS (no registers, rows past the sample end read as zero),
-// double-buffered so that step t+1 (or the next unit's first step) loads
-// while step t computes; one barrier per step.  K and V rows are stored
+// destination is LDS (no registers, rows past the sample end read as zero)
+// into a ring of NS stages: a producer cursor runs ahead of the step being
+// computed, across unit boundaries, and each step waits only for its own
+// loads (per-wave counts); one barrier per step.  With three stages or more
+// the steps are software-pipelined: the S^T MFMAs of step t+1 are issued
+// between the exponentials of step t's softmax, then P V of step t.  K and V rows are stored
 // permuted within each 32-key block (RowLoader PERM), which makes the 16
 // scores a lane holds 16 consecutive keys: the lane's bias values are then
 // two aligned 16-byte LDS reads.  The key-split partials of one query group
@@ -34,6 +37,7 @@
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
+#include "ring.hpp"
 
 namespace jattn {
 
@@ -52,6 +56,14 @@ struct Fwd2Shape {
   using BT = PadTile<BN, 1>;  // bias rows: pitch = 16 (mod 256) bytes, 16-byte reads conflict-free
   static constexpr int B_BYTES = BIAS ? BT::template bytes<BM>() : 0;
   static constexpr int STAGE = K_BYTES + V_BYTES + B_BYTES;
+  // ring depth: up to four stages (three steps in flight beside the one computed)
+  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : NS_FIT;
+  static_assert(NS >= 2, "two stages at least");
+  // LDS-destination load instructions of one step (whole workgroup)
+  static constexpr int KNI = KT::template ninst<BN>();
+  static constexpr int VNI = VT::template ninst<BN>();
+  static constexpr int BNI = BIAS ? BT::template ninst<BM>() : 0;
   // The key-split partials of O (key blocks 1..WK-1) are summed through the
   // stage of the unit's last step, DP 32-column blocks of D per pass; their
   // m, l, l_rounded go first.
@@ -62,18 +74,21 @@ struct Fwd2Shape {
   // extra barriers: short-key units are often a single step), else passes
   // through the free stage.
   static constexpr int OWN = STATS + COMB_PER_D * ND;
-  static constexpr bool COMB_IN_STAGE = WK > 1 && 2 * STAGE + OWN > 160 * 1024;
+  static constexpr bool COMB_IN_STAGE = WK > 1 && NS * STAGE + OWN > 160 * 1024;
   static_assert(!COMB_IN_STAGE || DP_FIT >= 1, "combine pass does not fit a stage");
   static constexpr int DP = !COMB_IN_STAGE || DP_FIT >= ND ? ND : (DP_FIT >= 2 && ND % 2 == 0 ? 2 : 1);
   static constexpr int EXTRA = (WK > 1 && !COMB_IN_STAGE) ? OWN : 0;
-  static constexpr int SMEM = 2 * STAGE + EXTRA;
+  static constexpr int SMEM = NS * STAGE + EXTRA;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
 template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
 __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   using Sh = Fwd2Shape<D, WQ, WK, BIAS>;
-  constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW;
+  constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW, NS = Sh::NS;
+  // software pipeline across steps when the ring holds three stages or more
+  constexpr bool PIPE = NS >= 3;
+  constexpr int LOOK = PIPE ? NS - 2 : NS - 1;  // productions in flight at an acquisition
   constexpr bool SOFTMAX = (ACT == kSoftmax);
   constexpr float kLazy = 8.0f;  // rescale only when a row max grows by > 2^8
 
@@ -82,8 +97,8 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   const int wq = wave % WQ, wk = wave / WQ;
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_begin = uniform(a.worker_off[worker]);
-  const int u_end = uniform(a.worker_off[worker + 1]);
+  const int u_begin = sload1(a.worker_off, worker);
+  const int u_end = sload1(a.worker_off, worker + 1);
   const int HD = a.H * D;
 
   auto stage_k = [&](int s) { return smem + s * Sh::STAGE; };
@@ -97,23 +112,24 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   BiasLoader<BN, 1, BM, NW> bload;
   kload.init(wave, lane, HD);
   vload.init(wave, lane, HD);
+  static_assert(decltype(kload)::NI == Sh::KNI && decltype(vload)::NI == Sh::VNI &&
+                    (!BIAS || decltype(bload)::NI == Sh::BNI),
+                "the ring's per-step counts are the loaders' instruction counts");
 
+  // Unit record: sample fields only (three are live at once: producer,
+  // current, next); descriptors are rebuilt where they are used.
   struct UnitInfo {
     int b, h, qt, n;
     Sample s;
-    i32x4 rk, rv;  // descriptors at row 0 of this (sample, head)
   };
   auto fetch = [&](int u) {
     UnitInfo x;
-    const i32x4 un = load_unit(a.units, u);
+    const i32x4 un = sload4(a.units, u);
     x.b = un[0];
     x.h = un[1];
     x.qt = un[2];
     x.n = un[3];
-    x.s = load_sample(a.samples, x.b);
-    const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D;
-    x.rk = rsrc_words(reinterpret_cast<const bf16*>(a.k) + kvo, 0);
-    x.rv = rsrc_words(reinterpret_cast<const bf16*>(a.v) + kvo, 0);
+    x.s = sload_sample(a.samples, x.b);
     return x;
   };
   // First element of the unit's (sample, head) bias block.  Derived where it
@@ -124,24 +140,6 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   // key tile of step t (a windowed unit starts at its window's first tile)
   auto key_tile = [&](const UnitInfo& x, int t) {
     return WIN ? window_first_step(x.qt * BM, a.win_l, BN) + t : t;
-  };
-  // issue the HBM -> LDS loads of step t of unit x into stage st: the K and V
-  // descriptors start at the step's first key row and end at the sample end
-  auto issue_step = [&](const UnitInfo& x, int t, int st) {
-    const uint32_t sb = smem_lds + st * Sh::STAGE;
-    const int kt = key_tile(x, t);
-    const int64_t row0 = (int64_t)kt * BN;
-    const int64_t rec = (int64_t)(x.s.lk - kt * BN) * HD * 2;
-    kload.issue(sb, rsrc_at(x.rk, row0 * HD * 2, rec), wave);
-    vload.issue(sb + Sh::K_BYTES, rsrc_at(x.rv, row0 * HD * 2, rec), wave);
-    if constexpr (BIAS) {
-      // rows qt*BM .. of the bias block, keys t*BN ..; the offsets follow lk
-      if (t == 0) bload.init(wave, lane, x.s.lk);
-      const int64_t e0 = bias_elem0(x);
-      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
-      const i32x4 rb = rsrc_words(reinterpret_cast<const bf16*>(a.bias) + e0, 0);
-      bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, rsrc_at(rb, off, (a.bias_elems - e0) * 2 - off), wave);
-    }
   };
   // Q fragments (B operand) of this wave's 32 rows, straight into registers
   auto load_q = [&](const UnitInfo& x, bf16x8* qf) {
@@ -154,11 +152,81 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
   };
 
   if (u_begin >= u_end) return;
+
+  // ---- producer: the worker's steps in order, LOOK ahead of the consumer ----
+  // Each production moves one step's K and V rows (and bias tile) into a
+  // stage.  The descriptors start at the step's first key row and end at the
+  // sample end (rows past it read as zero); they are set up once per unit and
+  // advanced by a constant per step.
+  const int step_ops = loads_of(Sh::KNI, wave, NW) + loads_of(Sh::VNI, wave, NW) + loads_of(Sh::BNI, wave, NW);
+  constexpr int MIN_OPS = loads_of(Sh::KNI, NW - 1, NW) + loads_of(Sh::VNI, NW - 1, NW) +
+                          loads_of(Sh::BNI, NW - 1, NW);  // the wave with the fewest loads
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  constexpr int32_t KV_STEP = BN * D * 2;  // bytes of one step's rows per head (rows are H heads apart)
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Walker<false> wk_k, wk_v;  // K and V rows of the next step
+  Walker<true> wk_b;         // bias rows of the next step
+  auto start_unit = [&](const UnitInfo& x) {
+    const int64_t kvo = ((int64_t)x.s.k0 * a.H + x.h) * D * 2;
+    const int64_t row0 = (int64_t)key_tile(x, 0) * BN;
+    const int64_t rec = ((int64_t)x.s.lk - row0) * HD * 2;
+    wk_k.start(reinterpret_cast<const char*>(a.k) + kvo, row0 * HD * 2, rec);
+    wk_v.start(reinterpret_cast<const char*>(a.v) + kvo, row0 * HD * 2, rec);
+    if constexpr (BIAS) {
+      // rows qt*BM .. of the bias block, keys from row0; the offsets follow lk
+      bload.init(wave, lane, x.s.lk);
+      const int64_t e0 = bias_elem0(x);
+      const int64_t off = ((int64_t)x.qt * BM * x.s.lk + row0) * 2;
+      wk_b.start(reinterpret_cast<const char*>(a.bias) + e0 * 2, off, (a.bias_elems - e0) * 2 - off);
+    }
+  };
+  UnitInfo pinfo = fetch(u_begin);
+  pn = pinfo.n;
+  if (pn > 0) start_unit(pinfo);
+  VmLedger<LOOK, WAIT_N> ring;
+  auto produce = [&]() {
+    if (pt >= pn && pu < u_end) {
+      // next unit with steps (units without keys have none)
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      const uint32_t sb = smem_lds + pst * Sh::STAGE;
+      kload.issue(sb, wk_k.words(), wave);
+      vload.issue(sb + Sh::K_BYTES, wk_v.words(), wave);
+      if constexpr (BIAS) bload.issue(sb + Sh::K_BYTES + Sh::V_BYTES, wk_b.words(), wave);
+      wk_k.advance(KV_STEP * a.H);
+      wk_v.advance(KV_STEP * a.H);
+      if constexpr (BIAS) wk_b.advance(BN * 2);
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
+  };
+  // the step computed next is the oldest production in flight
+  auto acquire = [&]() {
+    ring.wait_oldest();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // its tiles are in LDS; every wave is done with the stage produce() refills
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   UnitInfo cur = fetch(u_begin);
   bf16x8 qf[NKK];
   load_q(cur, qf);
-  int stage = 0;
-  if (cur.n > 0) issue_step(cur, 0, 0);
+  // the first unit's Q has landed before anything else is issued: every later
+  // Q load is followed by visible stores, so the compiler's own wait for it
+  // at a unit's first step leaves the ring in flight
+  wait_vmcnt<0>();
+  for (int j = 0; j < LOOK; ++j) produce();
+  int stage = 0;  // stage of the step whose softmax comes next
 
   for (int u = u_begin; u < u_end; ++u) {
     const bool has_next = u + 1 < u_end;
@@ -171,23 +239,31 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
     float m_run = 0.0f, l_run = 0.0f, lr_run = 0.0f;
     bool pad_drop = false;  // this row dropped its padded keys (see the guard below)
+    const int kb = wk * 32;  // this wave's key block inside a step
 
-    // One K/V step.  FIRST (step 0) starts the running max at the step's
-    // max; later steps rescale lazily.  Separate instances keep the
-    // accumulators in place across the rescale branch.
-    auto step = [&](auto first_tag, int t) {
+    // S^T of the step in stage st, all MFMAs at once
+    auto s_all = [&](int st) {
+      const char* kt = stage_k(st);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s = Elem<bf16>::mma(rows_frag<D, 1>(kt, kb + l32, kk, g), qf[kk], s);
+      return s;
+    };
+
+    // Softmax (or activation) of step t from its scores sacc and the bias
+    // tile in stage st: P into pf (and pl), the running max, sums and O
+    // rescaled.  FIRST (step 0) starts the running max at the step's max;
+    // later steps rescale lazily.  LAST (step n-1) holds the keys past the
+    // sample end.  mm(c), c = 0 .. NKK-1, is called between chunks of the
+    // exponential (or activation) work, one MFMA of the next step's S^T per
+    // call, so that the matrix core runs beside this VALU work; a
+    // scheduling fence after each chunk keeps that order.
+    auto soft = [&](auto first_tag, auto last_tag, int t, int st, const f32x16& sacc, auto&& mm, bf16x8* pf,
+                    bf16x8* pl) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      wait_vmcnt0();
-      __syncthreads();  // step t is in LDS; every wave is done with step t-1
-      if (t + 1 < n) {
-        issue_step(cur, t + 1, stage ^ 1);
-      } else if (has_next && nxt.n > 0) {
-        issue_step(nxt, 0, stage ^ 1);
-      }
-      const char* kt = stage_k(stage);
-      const char* vt = stage_v(stage);
-      const int kb = wk * 32;  // this wave's key block inside the step
-      const int key0 = key_tile(cur, t) * BN + kb;  // its first key
+      constexpr bool LAST = decltype(last_tag)::value;
+      constexpr int PER = 16 / NKK;  // elements of P per interleaved MFMA
+      const int key0 = key_tile(cur, t) * BN + kb;  // first key of this wave's block
       // window mask of this wave's 32x32 block (slot keys as described below)
       auto mask = [&](float* v, float fill) {
         const Window w{a.win_l, a.win_r, cur.s.lq, cur.s.lk};
@@ -199,20 +275,14 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
         }
       };
 
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sacc = Elem<bf16>::mma(rows_frag<D, 1>(kt, kb + l32, kk, g), qf[kk], sacc);
-      // Q is dead after the last S^T of the unit: fetch the next unit's rows
-      if (t + 1 == n && has_next) load_q(nxt, qf);
-
       // with a bias, slot i of this lane holds key t*BN + kb + 16g + i of
       // query row qt*BM + wq*32 + l32 (else key t*BN + kb + acc_row(i, g))
       float p[16];
       if constexpr (BIAS) {
-        const char* bt = stage_b(stage) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
+        const char* bt = stage_b(st) + (wq * 32 + l32) * Sh::BT::PITCH + (kb + 16 * g) * 2;
         bf16x8_to_f32(bt, p);
         bf16x8_to_f32(bt + 16, p + 8);
-        if (t + 1 == n) {
+        if constexpr (LAST) {
           // keys past the sample end carry the next row's bias: they must add
           // nothing (the subtraction below assumes a zero score)
           const int rem = cur.s.lk - (key0 + 16 * g);
@@ -229,7 +299,6 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           }
         }
       }
-      bf16x8 pf[2], pl[2];
       if constexpr (SOFTMAX) {
         // scores in log2 units relative to the running max: x - m
         float mx = -INFINITY;
@@ -239,7 +308,7 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           p[i] = fmaf(sacc[i], a.scale_log2, c);
         }
         if constexpr (WIN) mask(p, -INFINITY);
-        if constexpr (!WIN) {
+        if constexpr (!WIN && LAST) {
           // Guard of the subtraction scheme.  Keys past the sample end score
           // 0 in this last step.  When the row's best valid score is below 0
           // (log2 units), their exp terms would dominate the row sum and the
@@ -250,12 +319,12 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           // (earlier steps reach at least m_run), so it errs towards dropping,
           // which is exact too.
           const int rem = cur.s.lk - key0;  // valid keys of this wave's 32-key block
-          if (t + 1 == n && rem > 0 && rem < 32) {
-            float vm = -INFINITY;
+          if (rem > 0 && rem < 32) {
+            float vmax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) vm = (BIAS ? 16 * g + i : acc_row(i, g)) < rem ? fmaxf(vm, p[i]) : vm;
-            vm = wave_xor32_max(vm);
-            pad_drop = (FIRST ? vm : m_run + fmaxf(vm, 0.0f)) < 0.0f;
+            for (int i = 0; i < 16; ++i) vmax = (BIAS ? 16 * g + i : acc_row(i, g)) < rem ? fmaxf(vmax, p[i]) : vmax;
+            vmax = wave_xor32_max(vmax);
+            pad_drop = (FIRST ? vmax : m_run + fmaxf(vmax, 0.0f)) < 0.0f;
             if (pad_drop) {
 #pragma unroll
               for (int i = 0; i < 16; ++i) p[i] = (BIAS ? 16 * g + i : acc_row(i, g)) < rem ? p[i] : -INFINITY;
@@ -284,61 +353,144 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) p[i] -= delta;
           }
         }
+        // exponentials, row sums and the bf16 operands, interleaved with
+        // the next step's MFMAs.  The PV MFMA sees P rounded to bf16; the
+        // output is normalised by the sum of exactly those values
+        // (v_dot2_f32_bf16 against ones).
         float rs = 0.0f, rsr = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(p[i]);
-          rs += p[i];
-        }
-        // the PV MFMA sees P rounded to bf16; the output is normalised by the
-        // sum of exactly those values (v_dot2_f32_bf16 against ones)
         const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          pf[st] = pack8(&p[st * 8]);
+        for (int c = 0; c < NKK; ++c) {
+          mm(c);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            rsr = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[st][2 * j], pf[st][2 * j + 1]}, ones, rsr, false);
+          for (int j = 0; j < PER; ++j) {
+            const int i = c * PER + j;
+            p[i] = fast_exp2(p[i]);
+            rs += p[i];
+          }
+          if ((c + 1) * PER % 8 == 0) {
+            const int s8 = (c + 1) * PER / 8 - 1;
+            pf[s8] = pack8(&p[s8 * 8]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              rsr = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[s8][2 * j], pf[s8][2 * j + 1]}, ones, rsr, false);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         l_run += rs;
         lr_run += rsr;
       } else {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = BIAS ? p[i] + sacc[i] * a.scale : sacc[i] * a.scale;
-          p[i] = act_fwd(ACT, x);
+        for (int c = 0; c < NKK; ++c) {
+          mm(c);
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const int i = c * PER + j;
+            const float x = BIAS ? p[i] + sacc[i] * a.scale : sacc[i] * a.scale;
+            p[i] = act_fwd(ACT, x);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (WIN) mask(p, 0.0f);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          pf[st] = pack8(&p[st * 8]);
+        for (int s8 = 0; s8 < 2; ++s8) {
+          pf[s8] = pack8(&p[s8 * 8]);
           if constexpr (SPLIT) {
             float r8[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) r8[j] = p[st * 8 + j] - (float)pf[st][j];
-            pl[st] = pack8(r8);
+            for (int j = 0; j < 8; ++j) r8[j] = p[s8 * 8 + j] - (float)pf[s8][j];
+            pl[s8] = pack8(r8);
           }
         }
       }
+    };
 
+    // O^T += V^T P^T from the V tile in stage st
+    auto pv = [&](int st, const bf16x8* pf, const bf16x8* pl) {
+      const char* vt = stage_v(st);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int s8 = 0; s8 < 2; ++s8) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const bf16x8 vf = trans_frag<D, 2>(vt, wk, st, d * 32, lane);
-          oacc[d] = Elem<bf16>::mma(vf, pf[st], oacc[d]);
+          const bf16x8 vf = trans_frag<D, 2>(vt, wk, s8, d * 32, lane);
+          oacc[d] = Elem<bf16>::mma(vf, pf[s8], oacc[d]);
           // split operands matter for the activation path only: softmax
           // already normalises by the sum of the rounded P
-          if constexpr (SPLIT && !SOFTMAX) oacc[d] = Elem<bf16>::mma(vf, pl[st], oacc[d]);
+          if constexpr (SPLIT && !SOFTMAX) oacc[d] = Elem<bf16>::mma(vf, pl[s8], oacc[d]);
         }
       }
-      stage ^= 1;
     };
-    if (n > 0) {
-      step(std::true_type{}, 0);
-      for (int t = 1; t < n; ++t) step(std::false_type{}, t);
-    }
+    auto no_mm = [](int) {};
+    auto next_stage = [&](int st) { return st + 1 == NS ? 0 : st + 1; };
 
+    if constexpr (PIPE) {
+      // Software pipeline: S^T of step t+1 runs on the matrix core while the
+      // VALU works on the softmax of step t; then P V of step t.  Two stages
+      // are in use at once (t and t+1), so the producer runs NS - 2 ahead.
+      // LAST loads the next unit's Q (free once the unit's last S^T is done);
+      // it is the only instance that does, so the loop over the other steps
+      // carries no register loads in flight and the compiler puts no vmcnt
+      // wait of its own into it (such a wait would count only the loads it
+      // can see and drain the whole ring).
+      auto step = [&](auto first_tag, auto last_tag, int t, f32x16& sacc) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        bf16x8 pf[2], pl[2];
+        if constexpr (LAST) {
+          if (has_next) load_q(nxt, qf);
+          soft(first_tag, last_tag, t, stage, sacc, no_mm, pf, pl);
+        } else {
+          acquire();  // step t+1
+          produce();
+          const char* kn = stage_k(next_stage(stage));
+          f32x16 snx = f32x16{};
+          bf16x8 ka[NKK];
+          ka[0] = rows_frag<D, 1>(kn, kb + l32, 0, g);
+          if constexpr (NKK > 1) ka[1] = rows_frag<D, 1>(kn, kb + l32, 1, g);
+          auto mm = [&](int c) {
+            snx = Elem<bf16>::mma(ka[c], qf[c], snx);
+            if (c + 2 < NKK) ka[c + 2] = rows_frag<D, 1>(kn, kb + l32, c + 2, g);
+          };
+          soft(first_tag, last_tag, t, stage, sacc, mm, pf, pl);
+          sacc = snx;
+        }
+        pv(stage, pf, pl);
+        stage = next_stage(stage);
+      };
+      if (n > 0) {
+        acquire();  // step 0
+        produce();
+        f32x16 sacc = s_all(stage);
+        if (n == 1) {
+          step(std::true_type{}, std::true_type{}, 0, sacc);
+        } else {
+          step(std::true_type{}, std::false_type{}, 0, sacc);
+          for (int t = 1; t + 1 < n; ++t) step(std::false_type{}, std::false_type{}, t, sacc);
+          step(std::false_type{}, std::true_type{}, n - 1, sacc);
+        }
+      }
+    } else {
+      // one stage in use at a time: acquire, S^T, softmax, P V
+      auto step = [&](auto first_tag, auto last_tag, int t) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        acquire();
+        produce();
+        const f32x16 sacc = s_all(stage);
+        if (LAST && has_next) load_q(nxt, qf);
+        bf16x8 pf[2], pl[2];
+        soft(first_tag, last_tag, t, stage, sacc, no_mm, pf, pl);
+        pv(stage, pf, pl);
+        stage = next_stage(stage);
+      };
+      if (n == 1) {
+        step(std::true_type{}, std::true_type{}, 0);
+      } else if (n > 1) {
+        step(std::true_type{}, std::false_type{}, 0);
+        for (int t = 1; t + 1 < n; ++t) step(std::false_type{}, std::false_type{}, t);
+        step(std::false_type{}, std::true_type{}, n - 1);
+      }
+    }
     // ---- epilogue ----
     if constexpr (SOFTMAX) {
       l_run = wave_xor32_sum(l_run);
@@ -366,14 +518,16 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       }
     }
     const int qrow = cur.qt * BM + wq * 32 + l32;
-    TO* orow = reinterpret_cast<TO*>(a.o) + ((int64_t)(cur.s.q0 + qrow) * a.H + cur.h) * D;
     const bool valid_row = qrow < cur.s.lq;
     const bool has_keys = cur.s.lk > 0;
 
     if constexpr (WK > 1) {
-      // stage that held the last step is free once every wave passes this barrier
+      // the stage of the unit's last step (the one before `stage`) is free
+      // once every wave passes this barrier: no load refills it before the
+      // next acquisition's barrier
       __syncthreads();
-      char* free_stage = Sh::COMB_IN_STAGE ? smem + (stage ^ 1) * Sh::STAGE : smem + 2 * Sh::STAGE;
+      char* free_stage =
+          Sh::COMB_IN_STAGE ? smem + (stage == 0 ? NS - 1 : stage - 1) * Sh::STAGE : smem + NS * Sh::STAGE;
       float* ps = reinterpret_cast<float*>(free_stage);
       float* po = reinterpret_cast<float*>(free_stage + Sh::STATS);
       // element (row r of the 32-column block dl of a pass, query l32) of a
@@ -434,29 +588,43 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       }
     }
 
-    if (wk == 0 && valid_row) {
+    if (wk == 0) {
+      // buffer stores issued by every lane (rows past the sample end at an
+      // out-of-range offset), so that the count the ring's waits rely on
+      // does not depend on the data; they stay in flight across later waits
       float inv = 1.0f;
       if constexpr (SOFTMAX) inv = has_keys ? 1.0f / lr_run : 0.0f;
+      const rsrc_t ro = make_rsrc(reinterpret_cast<const TO*>(a.o) + ((int64_t)cur.s.q0 * a.H + cur.h) * D,
+                                  (uint32_t)cur.s.lq * HD * (uint32_t)sizeof(TO));
+      const uint32_t vrow = valid_row ? (uint32_t)(qrow * HD) * (uint32_t)sizeof(TO) : 0x80000000u;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          store4<TO>(orow + d * 32 + i4 * 8 + g * 4, oacc[d][i4 * 4] * inv, oacc[d][i4 * 4 + 1] * inv,
-                     oacc[d][i4 * 4 + 2] * inv, oacc[d][i4 * 4 + 3] * inv);
-      if (SOFTMAX && a.lse != nullptr && g == 0)
-        a.lse[((int64_t)cur.s.q0 + qrow) * a.H + cur.h] = has_keys ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+          buf_store4<TO>(ro, vrow + (uint32_t)(d * 32 + i4 * 8 + g * 4) * (uint32_t)sizeof(TO),
+                         oacc[d][i4 * 4] * inv, oacc[d][i4 * 4 + 1] * inv, oacc[d][i4 * 4 + 2] * inv,
+                         oacc[d][i4 * 4 + 3] * inv);
+      ring.counted(ND * 4);
+      if (SOFTMAX && a.lse != nullptr) {
+        const rsrc_t rl = make_rsrc(a.lse + (int64_t)cur.s.q0 * a.H + cur.h, (uint32_t)cur.s.lq * a.H * 4);
+        const float lse = has_keys ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl,
+                                              valid_row && g == 0 ? (uint32_t)qrow * a.H * 4 : 0x80000000u, 0, 0);
+        ring.counted(1);
+      }
     }
 
-    if (has_next) {
-      if (n == 0) load_q(nxt, qf);  // a unit without keys issued no prefetch
-      if (n == 0 && nxt.n > 0) {
-        wait_vmcnt0();
-        __syncthreads();  // nobody reads LDS in a keyless unit, but keep stage order
-        issue_step(nxt, 0, stage);
-      }
+    if (has_next && n == 0) {
+      // a unit without keys did not load the next Q; waiting here (units
+      // without keys are rare) keeps this path from putting a wait that
+      // drains the ring into every unit's first step
+      load_q(nxt, qf);
+      wait_vmcnt<0>();
     }
     cur = nxt;
   }
+  // every production was acquired; only stores can still be in flight
+  wait_vmcnt<0>();
 }
 
 }  // namespace jattn

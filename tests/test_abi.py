@@ -103,9 +103,13 @@ def test_plan_create_rejects(lib, kw, qo, ko, code):
 
 
 @pytest.mark.parametrize("kw,L,ok", [
-    # one sample's rows must span < 2^31 bytes (H * D * 2 = 512 bytes a row)
+    # one sample's rows must span < 2^31 bytes (H * D * 2 = 512 bytes a bf16 row) ...
     (dict(B=1, H=2, D=128), (1 << 22) - 1, True),
     (dict(B=1, H=2, D=128), 1 << 22, False),
+    # ... in its widest type: fp32 outputs or gradients make a row 1024 bytes
+    (dict(B=1, H=2, D=128, out_dtype=B.JATTN_F32), (1 << 21) - 1, True),
+    (dict(B=1, H=2, D=128, out_dtype=B.JATTN_F32), 1 << 21, False),
+    (dict(B=1, H=2, D=128, grad_dtype=B.JATTN_F32), 1 << 21, False),
     # a head's bf16 bias block must span < 2^30 bytes: 23170^2 * 2 < 2^30 <= 23171^2 * 2
     (dict(B=1, has_bias=1), 23170, True),
     (dict(B=1, has_bias=1), 23171, False),
