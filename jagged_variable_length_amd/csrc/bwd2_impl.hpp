@@ -152,14 +152,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   };
 
   // ---- producer: the loads of one step into one stage ----
-  // producer cursor: next (unit, step) to load; units without steps are skipped
-  int pu = u_begin, pt = 0, pst = 0;
-  Unit pinfo;
-  if (pu < u_end) pinfo = fetch(pu);
-  // prepare() advances the cursor and builds the descriptors of the next
-  // step; produce() issues its loads (issue_slot, one per load).  With no
-  // step left, the descriptors have no records and the loads write zeros
-  // into a stage nobody reads.
+  // The producer cursor (next unit and step to load; units without steps are
+  // skipped) runs NS - 2 productions ahead of the step being acquired.  The
+  // descriptors of the Q, dO, row-statistic and bias rows are set up once
+  // per unit and advanced by a constant per step.
   struct StepDMA {
     uint32_t sb;    // LDS byte address of the stage
     i32x4 rq, rdo;  // Q, dO rows of the step
@@ -171,57 +167,50 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   constexpr int NSLOT = 2 * NJQ + (SOFTMAX ? 1 : 0) + NJB;
   static_assert(Sh::NRS <= NW, "one row-stat load per wave at most");
   constexpr int S_OPS = DBIAS != 0 ? 16 : 0;  // dBias stores per step
-  // vector memory operations this wave issues per step
+  // vector memory operations this wave issues per step, and the fewest any wave issues
   const int step_ops = 2 * loads_of(Sh::QNI, wave, NW) + loads_of(Sh::NRS, wave, NW) + loads_of(Sh::BNI, wave, NW);
-  // Vector memory operations this wave has issued, and marks after the
-  // loads of the two most recently produced steps: produce() runs once per
-  // acquisition (after NS - 2 initial calls), so the step being acquired is
-  // the (NS - 2)-th latest.
-  int issued = 0, m1 = 0, m2 = 0;
-  auto prepare = [&]() __attribute__((always_inline)) {
-    while (pu < u_end && pt >= pinfo.n) {
-      ++pu;
-      pt = 0;
-      if (pu < u_end) pinfo = fetch(pu);
-    }
-    const bool active = pu < u_end;
-    const Unit& x = pinfo;
-    const int t = pt;
-    StepDMA d;
-    d.sb = smem_lds + pst * Sh::STAGE;
-    const int r0 = step_row0(x, t);
-    const int64_t rec = active ? (int64_t)(x.s.lq - r0) * HD * 2 : 0;
-    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D;  // first row of the step
-    d.rq = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_q) + qo, 0), 0, rec);
-    d.rdo = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_dout) + qo, 0), 0, rec);
+  constexpr int MIN_OPS =
+      2 * loads_of(Sh::QNI, NW - 1, NW) + loads_of(Sh::NRS, NW - 1, NW) + loads_of(Sh::BNI, NW - 1, NW);
+  constexpr int LOOK = NS - 2;  // productions in flight at an acquisition
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  VmLedger<LOOK, WAIT_N> ring;
+
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Unit pinfo;
+  Walker<false> w_q, w_do, w_rs;  // Q, dO rows and this wave's row-stat rows of the next step
+  Walker<true> w_b;               // bias rows of the next step
+  int brows = 0;                  // bias rows inside the sample from the next step's first row
+  int64_t bstep = 0;              // bytes between consecutive steps' bias rows
+  auto start_unit = [&](const Unit& x) __attribute__((always_inline)) {
+    const int r0 = step_row0(x, 0);
+    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D * 2;  // first row of step 0
+    const int64_t rec = (int64_t)(x.s.lq - r0) * HD * 2;
+    w_q.start(A_q, qo, rec);
+    w_do.start(A_dout, qo, rec);
     if constexpr (SOFTMAX) {
       // load `wave`: rows 64*(wave % (NRS/2)) .. of LSE (wave < NRS/2) or Di
       constexpr int HALF = Sh::NRS / 2;
       const int jj = wave < Sh::NRS ? wave : 0;
       const int rr = r0 + 64 * (jj % HALF);
-      const float* rsp = (jj < HALF ? A_lse2 : A_di) + ((int64_t)(x.s.q0 + rr) * H + x.h);
-      d.rs = rsrc_at(rsrc_words(rsp, 0), 0, active ? (int64_t)(x.s.lq - rr) * H * 4 : 0);
+      w_rs.start(jj < HALF ? A_lse2 : A_di, ((int64_t)(x.s.q0 + rr) * H + x.h) * 4, (int64_t)(x.s.lq - rr) * H * 4);
     }
     if constexpr (BIAS) {
-      // query rows t*QS .., keys kt*KT .. of the bias block; the offsets follow
+      // query rows from r0, keys kt*KT .. of the bias block; the offsets follow
       // lk; query rows past the sample end read as zero, like their Q, dO and
       // row statistics: their P is then finite and their dS exactly zero
-      if (active && t == 0) bload.init(wave, lane, x.s.lk);
+      bload.init(wave, lane, x.s.lk);
       const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
       const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
-      d.rb = rsrc_at(rsrc_words(reinterpret_cast<const bf16*>(A_bias) + e0, 0), off,
-                     active ? (A_bias_elems - e0) * 2 - off : 0);
-      d.brows = x.s.lq - r0;
+      w_b.start(reinterpret_cast<const char*>(A_bias) + e0 * 2, off, (A_bias_elems - e0) * 2 - off);
+      brows = x.s.lq - r0;
+      bstep = (int64_t)QS * x.s.lk * 2;
     }
-    issued += step_ops;
-    m2 = m1;
-    m1 = issued;
-    if (active) {
-      ++pt;
-      pst = pst + 1 == NS ? 0 : pst + 1;
-    }
-    return d;
   };
+  if (pu < u_end) {
+    pinfo = fetch(pu);
+    pn = pinfo.n;
+    if (pn > 0) start_unit(pinfo);
+  }
   // slot c (a compile-time constant after unrolling) of this wave's loads
   auto issue_slot = [&](const StepDMA& d, int c) __attribute__((always_inline)) {
     if (c < NJQ) {
@@ -238,16 +227,47 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
   };
   auto produce = [&]() __attribute__((always_inline)) {
-    const StepDMA d = prepare();
+    if (pt >= pn && pu < u_end) {
+      // next unit with steps
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      StepDMA d;
+      d.sb = smem_lds + pst * Sh::STAGE;
+      d.rq = w_q.words();
+      d.rdo = w_do.words();
+      if constexpr (SOFTMAX) d.rs = w_rs.words();
+      if constexpr (BIAS) {
+        d.rb = w_b.words();
+        d.brows = brows;
+      }
 #pragma unroll
-    for (int c = 0; c < NSLOT; ++c) issue_slot(d, c);
+      for (int c = 0; c < NSLOT; ++c) issue_slot(d, c);
+      w_q.advance(QS * HD * 2);
+      w_do.advance(QS * HD * 2);
+      if constexpr (SOFTMAX) w_rs.advance(QS * H * 4);
+      if constexpr (BIAS) {
+        w_b.advance(bstep);
+        brows -= QS;
+      }
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
   };
   // wait until the loads of the step being acquired have landed: everything
-  // issued after them may stay in flight (the K/V loads, which this count
+  // issued after them may stay in flight (the K/V loads, which the count
   // leaves out, only make the wait stricter)
   auto acquire = [&]() __attribute__((always_inline)) {
-    const int after = issued - (NS == 4 ? m2 : m1);
-    wait_vmcnt_le<0, 63>(max(min(after, 63), 0));
+    ring.wait_oldest();
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -415,7 +435,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)ds[i]), rdbr, voff, 0, 0);
       }
-      issued += S_OPS;
+      ring.counted(S_OPS);
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -552,7 +572,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (DBIAS != 0) issued += S_OPS;
+    if constexpr (DBIAS != 0) ring.counted(S_OPS);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       o.ph[s2] = pack8(&p[s2 * 8]);
@@ -594,7 +614,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   // ---- consumer ----
   if (u_begin >= u_end) return;
-  for (int j = 0; j < NS - 2; ++j) produce();
+  for (int j = 0; j < LOOK; ++j) produce();
   // first unit with steps: its K/V
   for (int u0 = u_begin; u0 < u_end; ++u0) {
     const Unit x0 = fetch(u0);
@@ -648,8 +668,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     store_unit(x, dkacc, dvacc, cs);
     if (x.n > 0) cs = cs + 1 == NS ? 0 : cs + 1;
   }
-  // loads issued past the last step (zero records) must land before the
-  // workgroup's LDS is released
+  // every production was acquired; only stores and register loads can still
+  // be in flight
   wait_vmcnt<0>();
 }
 

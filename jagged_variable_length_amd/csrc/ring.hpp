@@ -120,9 +120,9 @@ struct Walker {
     addr = (uint64_t)(uintptr_t)base + (uint64_t)off;
     left = (L)bytes_left;
   }
-  __device__ __forceinline__ void advance(int32_t bytes) {
-    addr += (uint64_t)(int64_t)bytes;
-    left -= bytes;
+  __device__ __forceinline__ void advance(int64_t bytes) {
+    addr += (uint64_t)bytes;
+    left -= (L)bytes;
   }
   __device__ __forceinline__ i32x4 words() const {
     int32_t n;
