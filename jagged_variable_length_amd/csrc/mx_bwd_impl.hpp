@@ -157,22 +157,53 @@ struct MxDkdvShape {
   static constexpr int OFF_DOT = OFF_QT + T::T_BYTES;
   static constexpr int OFF_RS = OFF_DOT + T::T_BYTES;  // LSE*log2e [64], Di [64]
   static constexpr int STAGE = OFF_RS + (SOFTMAX ? 512 : 0);
-  static constexpr int SMEM = 2 * STAGE;
-  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : NS_FIT;  // ring stages
+  static_assert(NS >= 2, "two stages at least");
+  static constexpr int SMEM = NS * STAGE;
 };
 
+// Unit record of the MXFP8 kernels: head, tile, steps, sample fields and the
+// sample's first row blocks of Q and K (entries 6 and 7 of its table entry),
+// read with scalar loads.
+struct MxUnit {
+  int h, tile, n;
+  Sample s;
+  int qblk0, kblk0;
+};
+__device__ __forceinline__ MxUnit mx_fetch(const int32_t* units, const int32_t* samples, int u) {
+  MxUnit x;
+  const i32x4 un = sload4(units, u);
+  x.h = un[1];
+  x.tile = un[2];
+  x.n = un[3];
+  x.s = sload_sample(samples, un[0]);
+  const i32x4 y = sload4(samples, 2 * un[0] + 1);
+  x.qblk0 = y[2];
+  x.kblk0 = y[3];
+  return x;
+}
+
+// Both gradient kernels: the tiles of a step travel HBM -> LDS into a ring of
+// NS stages filled by a producer cursor that runs NS - 1 steps ahead across
+// unit boundaries (descriptors set up once per unit, advanced per step; each
+// step waits only for its own loads, with per-wave counts); the register
+// operands of the next unit with steps are loaded in the last step of a unit
+// (its own instance, so the loop over the other steps carries no register
+// loads for the compiler to wait on); gradients are stored with buffer
+// stores from every lane, so the counts do not depend on the data.
 template <typename TG, int D, int ACT>
 __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
   constexpr bool SOFTMAX = (ACT == kSoftmax);
   using Sh = MxDkdvShape<D, SOFTMAX>;
   using Tl = MxBwdTiles<D>;
-  constexpr int NC = D / 64, ND = D / 32, KT = 128, QS = 64;
+  constexpr int NC = D / 64, ND = D / 32, KT = 128, QS = 64, NS = Sh::NS;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_begin = uniform(a.worker_off[worker]);
-  const int u_end = uniform(a.worker_off[worker + 1]);
+  const int u_begin = sload1(a.worker_off, worker);
+  const int u_end = sload1(a.worker_off, worker + 1);
   const int H = a.H, HD = H * D;
   const int64_t BLK = (int64_t)H * D * 32;
   const uint32_t smem_lds = lds_addr(smem);
@@ -180,56 +211,113 @@ __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
   rload.init(wave, lane, HD / 2);
   TLoader<D> tload;
   tload.init(wave, lane, BLK);
+  if (u_begin >= u_end) return;
+  auto fetch = [&](int u) { return mx_fetch(a.units, a.samples, u); };
 
-  for (int u = u_begin; u < u_end; ++u) {
-    const i32x4 un = load_unit(a.units, u);
-    const int b = un[0], h = un[1], kt = un[2], n = un[3];
-    const Sample s = load_sample(a.samples, b);
-    const i32x2 rb = reinterpret_cast<const i32x2*>(a.samples + 8 * b + 6)[0];
-    const int qblk0 = uniform(rb[0]), kblk0 = uniform(rb[1]);
-    const int nqb = (s.lq + 31) >> 5, nkb = (s.lk + 31) >> 5;
-    const int key = kt * KT + wave * 32 + l32;  // this lane's key (column of S)
-    const bool key_ok = key < s.lk;
-
-    // K and V rows of this wave's keys (B operands), their scale bytes
-    i32x8 kf[NC], vf[NC];
-    int ksc[NC], vsc[NC];
-    {
-      const int64_t base = ((int64_t)s.k0 * H + h) * D;
-      const rsrc_t rk = make_rsrc(a.k.codes + base, (uint32_t)s.lk * HD);
-      const rsrc_t rv = make_rsrc(a.v.codes + base, (uint32_t)s.lk * HD);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kf[c] = mx_row_regs(rk, (uint32_t)key * HD, c, g);
-        vf[c] = mx_row_regs(rv, (uint32_t)key * HD, c, g);
+  // ---- producer: Q, dO rows, their transposed tiles and the row statistics
+  // of query rows 64t .. of the unit's (sample, head) ----
+  constexpr int RNI = decltype(rload)::NI, TNI = Tl::T_NI;
+  const int step_ops = 2 * loads_of(RNI, wave, 4) + 2 * loads_of(TNI, wave, 4) + (SOFTMAX && wave < 2 ? 1 : 0);
+  constexpr int MIN_OPS = 2 * loads_of(RNI, 3, 4) + 2 * loads_of(TNI, 3, 4);  // wave 3: no row statistics
+  constexpr int LOOK = NS - 1;
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  VmLedger<LOOK, WAIT_N> ring;
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Walker<false> w_q, w_do, w_qt, w_dot, w_rs;
+  auto start_unit = [&](const MxUnit& x) {
+    const int64_t qo = ((int64_t)x.s.q0 * H + x.h) * D;
+    w_q.start(a.q.codes, qo, (int64_t)x.s.lq * HD);
+    w_do.start(a.dout.codes, qo, (int64_t)x.s.lq * HD);
+    // token blocks qblk0 + 2t, + 2t + 1; the descriptor ends with the sample's
+    // last block, so a block past it reads zero
+    const int nqb = (x.s.lq + 31) >> 5;
+    const int64_t vb = ((int64_t)x.qblk0 * H + x.h) * D * 32;
+    const int64_t vend = ((int64_t)(x.qblk0 + nqb - 1) * H + x.h + 1) * D * 32;
+    w_qt.start(a.q.codes_t, vb, vend - vb);
+    w_dot.start(a.dout.codes_t, vb, vend - vb);
+    // LSE * log2e (wave 0) or Di (wave 1); rows past the sample end read zero
+    if constexpr (SOFTMAX)
+      w_rs.start(wave == 0 ? a.lse2 : a.di, ((int64_t)x.s.q0 * H + x.h) * 4, (int64_t)x.s.lq * H * 4);
+  };
+  MxUnit pinfo = fetch(u_begin);
+  pn = pinfo.n;
+  if (pn > 0) start_unit(pinfo);
+  auto produce = [&]() {
+    if (pt >= pn && pu < u_end) {
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      const uint32_t sb = smem_lds + pst * Sh::STAGE;
+      rload.issue(sb, w_q.words(), wave);
+      rload.issue(sb + Sh::OFF_DO, w_do.words(), wave);
+      tload.issue(sb + Sh::OFF_QT, w_qt.words(), wave);
+      tload.issue(sb + Sh::OFF_DOT, w_dot.words(), wave);
+      if constexpr (SOFTMAX) {
+        if (wave < 2) lds_dma4(w_rs.words(), sb + Sh::OFF_RS + wave * 256, (uint32_t)lane * H * 4);
       }
-      const int kbk = kblk0 + min(kt * 4 + wave, nkb - 1);
-      const uint32_t kw = mx_scale_word<D>(a.k.scales, kbk, h, H);
-      const uint32_t vw = mx_scale_word<D>(a.v.scales, kbk, h, H);
+      w_q.advance((int64_t)QS * HD);
+      w_do.advance((int64_t)QS * HD);
+      w_qt.advance(2 * BLK);
+      w_dot.advance(2 * BLK);
+      if constexpr (SOFTMAX) w_rs.advance((int64_t)QS * H * 4);
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
+  };
+
+  // K and V rows of this wave's keys (B operands) and their scale bytes
+  i32x8 kf[NC], vf[NC];
+  int ksc[NC], vsc[NC];
+  auto load_kv = [&](const MxUnit& x) {
+    const int key = x.tile * KT + wave * 32 + l32;
+    const int64_t base = ((int64_t)x.s.k0 * H + x.h) * D;
+    const rsrc_t rk = make_rsrc(a.k.codes + base, (uint32_t)x.s.lk * HD);
+    const rsrc_t rv = make_rsrc(a.v.codes + base, (uint32_t)x.s.lk * HD);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        ksc[c] = scale_byte(kw, 2 * c + g);
-        vsc[c] = scale_byte(vw, 2 * c + g);
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = mx_row_regs(rk, (uint32_t)key * HD, c, g);
+      vf[c] = mx_row_regs(rv, (uint32_t)key * HD, c, g);
+    }
+    const int nkb = (x.s.lk + 31) >> 5;
+    const int kbk = x.kblk0 + min(x.tile * 4 + wave, nkb - 1);
+    const uint32_t kw = mx_scale_word<D>(a.k.scales, kbk, x.h, H);
+    const uint32_t vw = mx_scale_word<D>(a.v.scales, kbk, x.h, H);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      ksc[c] = scale_byte(kw, 2 * c + g);
+      vsc[c] = scale_byte(vw, 2 * c + g);
+    }
+  };
+  auto load_next_kv = [&](int from) {
+    for (int un = from; un < u_end; ++un) {
+      const MxUnit xn = fetch(un);
+      if (xn.n > 0) {
+        load_kv(xn);
+        break;
       }
     }
-    auto issue = [&](int t, int st) {
-      const uint32_t sb = smem_lds + st * Sh::STAGE;
-      const int64_t r0 = (int64_t)t * QS;
-      const int64_t rec = (int64_t)(s.lq - t * QS) * HD;
-      const int64_t qo = ((int64_t)s.q0 * H + h) * D;
-      rload.issue(sb, rsrc_at(rsrc_words(a.q.codes + qo, 0), r0 * HD, rec), wave);
-      rload.issue(sb + Sh::OFF_DO, rsrc_at(rsrc_words(a.dout.codes + qo, 0), r0 * HD, rec), wave);
-      tload.issue(sb + Sh::OFF_QT, ttile_rsrc<D>(a.q.codes_t, qblk0 + 2 * t, qblk0 + nqb - 1, h, H), wave);
-      tload.issue(sb + Sh::OFF_DOT, ttile_rsrc<D>(a.dout.codes_t, qblk0 + 2 * t, qblk0 + nqb - 1, h, H), wave);
-      if constexpr (SOFTMAX) {
-        if (wave < 2) {
-          // LSE * log2e (wave 0) or Di (wave 1) of the step's 64 query rows
-          const float* src = (wave == 0 ? a.lse2 : a.di) + ((int64_t)s.q0 + t * QS) * H + h;
-          lds_dma4(rsrc_at(rsrc_words(src, 0), 0, (int64_t)(s.lq - t * QS) * H * 4),
-                   sb + Sh::OFF_RS + wave * 256, (uint32_t)lane * H * 4);
-        }
-      }
-    };
+  };
+  // the first unit's K/V have landed before anything else is issued
+  load_next_kv(u_begin);
+  wait_vmcnt<0>();
+  for (int j = 0; j < LOOK; ++j) produce();
+  int stage = 0;
+
+  for (int u = u_begin; u < u_end; ++u) {
+    const MxUnit x = fetch(u);
+    const int n = x.n;
+    const int nqb = (x.s.lq + 31) >> 5;
+    const int key = x.tile * KT + wave * 32 + l32;  // this lane's key (column of S)
+    const bool key_ok = key < x.s.lk;
 
     f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
@@ -237,22 +325,20 @@ __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
       dkacc[d] = f32x16{};
       dvacc[d] = f32x16{};
     }
-    int stage = 0;
-    if (n > 0) {
-      __syncthreads();  // the previous unit is done with the LDS stages
-      issue(0, 0);
-    }
-    for (int t = 0; t < n; ++t) {
-      wait_vmcnt0();
-      __syncthreads();
-      if (t + 1 < n) issue(t + 1, stage ^ 1);
+    auto step = [&](auto last_tag, int t) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      ring.wait_oldest();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // step t is in LDS; every wave is done with the stage produce() refills
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
       const char* sb = smem + stage * Sh::STAGE;
       int qw[2], dw[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int blk = qblk0 + min(2 * t + qb, nqb - 1);
-        qw[qb] = (int)mx_scale_word<D>(a.q.scales, blk, h, H);
-        dw[qb] = (int)mx_scale_word<D>(a.dout.scales, blk, h, H);
+        const int blk = x.qblk0 + min(2 * t + qb, nqb - 1);
+        qw[qb] = (int)mx_scale_word<D>(a.q.scales, blk, x.h, H);
+        dw[qb] = (int)mx_scale_word<D>(a.dout.scales, blk, x.h, H);
       }
       // ---- S = Q K^T and dP = dO V^T; lane (key, g) holds queries qb*32 + acc_row(i, g) ----
       f32x16 sacc[2], pacc[2];
@@ -268,6 +354,8 @@ __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
           pacc[qb] = mx_mma(mx_frag(drow + c * 64, g), vf[c], pacc[qb], scale_byte(dw[qb], 2 * c + g), vsc[c]);
         }
       }
+      // K and V are free after the unit's last S/dP: the next unit with steps loads its own
+      if constexpr (LAST) load_next_kv(u + 1);
       // ---- P, dS ----
       float p[2][16], ds[2][16];
 #pragma unroll
@@ -292,9 +380,9 @@ __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
             p[qb][i] = fast_exp2(fmaf(sacc[qb][i], a.scale_log2, -lse2[i]));
             ds[qb][i] = p[qb][i] * (pacc[qb][i] - di[i]);
           } else {
-            const float x = sacc[qb][i] * a.scale;
-            p[qb][i] = act_fwd(ACT, x);
-            ds[qb][i] = act_grad(ACT, x) * pacc[qb][i];
+            const float xv = sacc[qb][i] * a.scale;
+            p[qb][i] = act_fwd(ACT, xv);
+            ds[qb][i] = act_grad(ACT, xv) * pacc[qb][i];
           }
           p[qb][i] = key_ok ? p[qb][i] : 0.0f;
           ds[qb][i] = key_ok ? ds[qb][i] : 0.0f;
@@ -321,23 +409,33 @@ __global__ __launch_bounds__(256, 1) void mx_dkdv_kernel(MxBwdArgs a) {
         dvacc[d] = mx_mma(mx_frag(sb + Sh::OFF_DOT + (d * 32 + l32) * Tl::TPITCH, g), pop, dvacc[d], ad, psc);
         dkacc[d] = mx_mma(mx_frag(sb + Sh::OFF_QT + (d * 32 + l32) * Tl::TPITCH, g), sop, dkacc[d], aq, ssc);
       }
-      stage ^= 1;
+      stage = stage + 1 == NS ? 0 : stage + 1;
+    };
+    if (n > 0) {
+      for (int t = 0; t + 1 < n; ++t) step(std::false_type{}, t);
+      step(std::true_type{}, n - 1);
     }
     // ---- store dK = scale * dK^T^T, dV: lane (key, g) holds features d*32 + acc_row(i, g) ----
-    if (key_ok) {
-      TG* dkrow = reinterpret_cast<TG*>(a.dk) + ((int64_t)(s.k0 + key) * H + h) * D;
-      TG* dvrow = reinterpret_cast<TG*>(a.dv) + ((int64_t)(s.k0 + key) * H + h) * D;
+    {
+      const int64_t base = ((int64_t)x.s.k0 * H + x.h) * D;
+      const uint32_t bytes = (uint32_t)x.s.lk * HD * (uint32_t)sizeof(TG);
+      const rsrc_t rdk = make_rsrc(reinterpret_cast<const TG*>(a.dk) + base, bytes);
+      const rsrc_t rdv = make_rsrc(reinterpret_cast<const TG*>(a.dv) + base, bytes);
+      const uint32_t vrow = key_ok ? (uint32_t)(key * HD) * (uint32_t)sizeof(TG) : 0x80000000u;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int col = d * 32 + i4 * 8 + g * 4;
-          store4<TG>(dkrow + col, a.scale * dkacc[d][i4 * 4], a.scale * dkacc[d][i4 * 4 + 1],
-                     a.scale * dkacc[d][i4 * 4 + 2], a.scale * dkacc[d][i4 * 4 + 3]);
-          store4<TG>(dvrow + col, dvacc[d][i4 * 4], dvacc[d][i4 * 4 + 1], dvacc[d][i4 * 4 + 2], dvacc[d][i4 * 4 + 3]);
+          const uint32_t off = vrow + (uint32_t)(d * 32 + i4 * 8 + g * 4) * (uint32_t)sizeof(TG);
+          buf_store4<TG>(rdk, off, a.scale * dkacc[d][i4 * 4], a.scale * dkacc[d][i4 * 4 + 1],
+                         a.scale * dkacc[d][i4 * 4 + 2], a.scale * dkacc[d][i4 * 4 + 3]);
+          buf_store4<TG>(rdv, off, dvacc[d][i4 * 4], dvacc[d][i4 * 4 + 1], dvacc[d][i4 * 4 + 2], dvacc[d][i4 * 4 + 3]);
         }
+      ring.counted(2 * ND * 4);
     }
   }
+  // every production was acquired; only stores can still be in flight
+  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -349,8 +447,10 @@ struct MxDqShape {
   static constexpr int OFF_V = T::R_BYTES;
   static constexpr int OFF_KT = 2 * T::R_BYTES;
   static constexpr int STAGE = OFF_KT + T::T_BYTES;
-  static constexpr int SMEM = 2 * STAGE;
-  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : NS_FIT;  // ring stages
+  static_assert(NS >= 2, "two stages at least");
+  static constexpr int SMEM = NS * STAGE;
 };
 
 template <typename TG, int D, int ACT>
@@ -358,13 +458,13 @@ __global__ __launch_bounds__(256, 1) void mx_dq_kernel(MxBwdArgs a) {
   constexpr bool SOFTMAX = (ACT == kSoftmax);
   using Sh = MxDqShape<D>;
   using Tl = MxBwdTiles<D>;
-  constexpr int NC = D / 64, ND = D / 32, BM = 128, BN = 64;
+  constexpr int NC = D / 64, ND = D / 32, BM = 128, BN = 64, NS = Sh::NS;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_begin = uniform(a.worker_off[worker]);
-  const int u_end = uniform(a.worker_off[worker + 1]);
+  const int u_begin = sload1(a.worker_off, worker);
+  const int u_end = sload1(a.worker_off, worker + 1);
   const int H = a.H, HD = H * D;
   const int64_t BLK = (int64_t)H * D * 32;
   const uint32_t smem_lds = lds_addr(smem);
@@ -372,95 +472,156 @@ __global__ __launch_bounds__(256, 1) void mx_dq_kernel(MxBwdArgs a) {
   rload.init(wave, lane, HD / 2);
   TLoader<D> tload;
   tload.init(wave, lane, BLK);
+  if (u_begin >= u_end) return;
+  auto fetch = [&](int u) { return mx_fetch(a.units, a.samples, u); };
 
-  for (int u = u_begin; u < u_end; ++u) {
-    const i32x4 un = load_unit(a.units, u);
-    const int b = un[0], h = un[1], qt = un[2], n = un[3];
-    const Sample s = load_sample(a.samples, b);
-    const i32x2 rb = reinterpret_cast<const i32x2*>(a.samples + 8 * b + 6)[0];
-    const int qblk0 = uniform(rb[0]), kblk0 = uniform(rb[1]);
-    const int nqb = (s.lq + 31) >> 5, nkb = (s.lk + 31) >> 5;
-    const int q = qt * BM + wave * 32 + l32;  // this lane's query row
+  // ---- producer: K, V rows and the transposed K tile of keys 64t .. ----
+  constexpr int RNI = decltype(rload)::NI, TNI = Tl::T_NI;
+  const int step_ops = 2 * loads_of(RNI, wave, 4) + loads_of(TNI, wave, 4);
+  constexpr int MIN_OPS = 2 * loads_of(RNI, 3, 4) + loads_of(TNI, 3, 4);
+  constexpr int LOOK = NS - 1;
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  VmLedger<LOOK, WAIT_N> ring;
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Walker<false> w_k, w_v, w_kt;
+  auto start_unit = [&](const MxUnit& x) {
+    const int64_t ko = ((int64_t)x.s.k0 * H + x.h) * D;
+    w_k.start(a.k.codes, ko, (int64_t)x.s.lk * HD);
+    w_v.start(a.v.codes, ko, (int64_t)x.s.lk * HD);
+    const int nkb = (x.s.lk + 31) >> 5;
+    const int64_t vb = ((int64_t)x.kblk0 * H + x.h) * D * 32;
+    const int64_t vend = ((int64_t)(x.kblk0 + nkb - 1) * H + x.h + 1) * D * 32;
+    w_kt.start(a.k.codes_t, vb, vend - vb);
+  };
+  MxUnit pinfo = fetch(u_begin);
+  pn = pinfo.n;
+  if (pn > 0) start_unit(pinfo);
+  auto produce = [&]() {
+    if (pt >= pn && pu < u_end) {
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      const uint32_t sb = smem_lds + pst * Sh::STAGE;
+      rload.issue(sb, w_k.words(), wave);
+      rload.issue(sb + Sh::OFF_V, w_v.words(), wave);
+      tload.issue(sb + Sh::OFF_KT, w_kt.words(), wave);
+      w_k.advance((int64_t)BN * HD);
+      w_v.advance((int64_t)BN * HD);
+      w_kt.advance(2 * BLK);
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
+  };
 
-    i32x8 qf[NC], df[NC];
-    int qsc[NC], dsc[NC];
-    float lse2 = 0.0f, di = 0.0f;
-    {
-      const int64_t base = ((int64_t)s.q0 * H + h) * D;
-      const rsrc_t rq = make_rsrc(a.q.codes + base, (uint32_t)s.lq * HD);
-      const rsrc_t rd = make_rsrc(a.dout.codes + base, (uint32_t)s.lq * HD);
+  // Q and dO rows of this lane's query (B operands), scale bytes, row statistics
+  i32x8 qf[NC], df[NC];
+  int qsc[NC], dsc[NC];
+  float lse2 = 0.0f, di = 0.0f;
+  auto load_rows = [&](const MxUnit& x) {
+    const int q = x.tile * BM + wave * 32 + l32;
+    const int64_t base = ((int64_t)x.s.q0 * H + x.h) * D;
+    const rsrc_t rq = make_rsrc(a.q.codes + base, (uint32_t)x.s.lq * HD);
+    const rsrc_t rd = make_rsrc(a.dout.codes + base, (uint32_t)x.s.lq * HD);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qf[c] = mx_row_regs(rq, (uint32_t)q * HD, c, g);
-        df[c] = mx_row_regs(rd, (uint32_t)q * HD, c, g);
-      }
-      const int qbk = qblk0 + min(qt * 4 + wave, nqb - 1);
-      const uint32_t qw = mx_scale_word<D>(a.q.scales, qbk, h, H);
-      const uint32_t dw = mx_scale_word<D>(a.dout.scales, qbk, h, H);
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = mx_row_regs(rq, (uint32_t)q * HD, c, g);
+      df[c] = mx_row_regs(rd, (uint32_t)q * HD, c, g);
+    }
+    const int nqb = (x.s.lq + 31) >> 5;
+    const int qbk = x.qblk0 + min(x.tile * 4 + wave, nqb - 1);
+    const uint32_t qw = mx_scale_word<D>(a.q.scales, qbk, x.h, H);
+    const uint32_t dw = mx_scale_word<D>(a.dout.scales, qbk, x.h, H);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qsc[c] = scale_byte(qw, 2 * c + g);
-        dsc[c] = scale_byte(dw, 2 * c + g);
-      }
-      if constexpr (SOFTMAX) {
-        // rows past the sample end read as zero
-        const uint32_t rec = (uint32_t)s.lq * H * 4;
-        lse2 = __uint_as_float(buf_load4(make_rsrc(a.lse2 + (int64_t)s.q0 * H + h, rec), (uint32_t)q * H * 4));
-        di = __uint_as_float(buf_load4(make_rsrc(a.di + (int64_t)s.q0 * H + h, rec), (uint32_t)q * H * 4));
+    for (int c = 0; c < NC; ++c) {
+      qsc[c] = scale_byte(qw, 2 * c + g);
+      dsc[c] = scale_byte(dw, 2 * c + g);
+    }
+    if constexpr (SOFTMAX) {
+      // rows past the sample end read as zero
+      const uint32_t rec = (uint32_t)x.s.lq * H * 4;
+      lse2 = __uint_as_float(buf_load4(make_rsrc(a.lse2 + (int64_t)x.s.q0 * H + x.h, rec), (uint32_t)q * H * 4));
+      di = __uint_as_float(buf_load4(make_rsrc(a.di + (int64_t)x.s.q0 * H + x.h, rec), (uint32_t)q * H * 4));
+    }
+  };
+  auto load_next_rows = [&](int from) {
+    for (int un = from; un < u_end; ++un) {
+      const MxUnit xn = fetch(un);
+      if (xn.n > 0) {
+        load_rows(xn);
+        break;
       }
     }
-    auto issue = [&](int t, int st) {
-      const uint32_t sb = smem_lds + st * Sh::STAGE;
-      const int64_t r0 = (int64_t)t * BN;
-      const int64_t rec = (int64_t)(s.lk - t * BN) * HD;
-      const int64_t ko = ((int64_t)s.k0 * H + h) * D;
-      rload.issue(sb, rsrc_at(rsrc_words(a.k.codes + ko, 0), r0 * HD, rec), wave);
-      rload.issue(sb + Sh::OFF_V, rsrc_at(rsrc_words(a.v.codes + ko, 0), r0 * HD, rec), wave);
-      tload.issue(sb + Sh::OFF_KT, ttile_rsrc<D>(a.k.codes_t, kblk0 + 2 * t, kblk0 + nkb - 1, h, H), wave);
-    };
+  };
+  // the first unit's rows have landed before anything else is issued
+  load_next_rows(u_begin);
+  wait_vmcnt<0>();
+  for (int j = 0; j < LOOK; ++j) produce();
+  int stage = 0;
+
+  for (int u = u_begin; u < u_end; ++u) {
+    const MxUnit x = fetch(u);
+    const int n = x.n;
+    const int nkb = (x.s.lk + 31) >> 5;
+    const int q = x.tile * BM + wave * 32 + l32;  // this lane's query row
+    // this unit's row statistics (the next unit's may load during its last step)
+    const float lse2_u = lse2, di_u = di;
 
     f32x16 dqacc[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) dqacc[d] = f32x16{};
-    int stage = 0;
-    if (n > 0) {
-      __syncthreads();
-      issue(0, 0);
-    }
-    for (int t = 0; t < n; ++t) {
-      wait_vmcnt0();
-      __syncthreads();
-      if (t + 1 < n) issue(t + 1, stage ^ 1);
+    auto step = [&](auto last_tag, int t) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      ring.wait_oldest();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // step t is in LDS; every wave is done with the stage produce() refills
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
       const char* sb = smem + stage * Sh::STAGE;
       int kw[2], vw[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int blk = kblk0 + min(2 * t + kb, nkb - 1);
-        kw[kb] = (int)mx_scale_word<D>(a.k.scales, blk, h, H);
-        vw[kb] = (int)mx_scale_word<D>(a.v.scales, blk, h, H);
+        const int blk = x.kblk0 + min(2 * t + kb, nkb - 1);
+        kw[kb] = (int)mx_scale_word<D>(a.k.scales, blk, x.h, H);
+        vw[kb] = (int)mx_scale_word<D>(a.v.scales, blk, x.h, H);
       }
       // ---- S^T = K Q^T, dP^T = V dO^T; lane (query, g) holds keys kb*32 + acc_row(i, g) ----
-      float ds[2][16];
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
         const char* krow = sb + Tl::RT::off(kb * 32 + l32, 0);
         const char* vrow = sb + Sh::OFF_V + Tl::RT::off(kb * 32 + l32, 0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          sacc = mx_mma(mx_frag(krow + c * 64, g), qf[c], sacc, scale_byte(kw[kb], 2 * c + g), qsc[c]);
-          pacc = mx_mma(mx_frag(vrow + c * 64, g), df[c], pacc, scale_byte(vw[kb], 2 * c + g), dsc[c]);
+          sacc[kb] = mx_mma(mx_frag(krow + c * 64, g), qf[c], sacc[kb], scale_byte(kw[kb], 2 * c + g), qsc[c]);
+          pacc[kb] = mx_mma(mx_frag(vrow + c * 64, g), df[c], pacc[kb], scale_byte(vw[kb], 2 * c + g), dsc[c]);
         }
+      }
+      // Q and dO are free after the unit's last S^T / dP^T: the next unit with steps loads its own
+      if constexpr (LAST) load_next_rows(u + 1);
+      float ds[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const int kbase = t * BN + kb * 32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float v;
           if constexpr (SOFTMAX) {
-            v = fast_exp2(fmaf(sacc[i], a.scale_log2, -lse2)) * (pacc[i] - di);
+            v = fast_exp2(fmaf(sacc[kb][i], a.scale_log2, -lse2_u)) * (pacc[kb][i] - di_u);
           } else {
-            v = act_grad(ACT, sacc[i] * a.scale) * pacc[i];
+            v = act_grad(ACT, sacc[kb][i] * a.scale) * pacc[kb][i];
           }
-          ds[kb][i] = kbase + acc_row(i, g) < s.lk ? v : 0.0f;  // keys past the end: none
+          ds[kb][i] = kbase + acc_row(i, g) < x.s.lk ? v : 0.0f;  // keys past the end: none
         }
       }
       // ---- dS to E4M3, one exponent per 32 x 32 block; dQ^T += K^T dS^T ----
@@ -477,18 +638,28 @@ __global__ __launch_bounds__(256, 1) void mx_dq_kernel(MxBwdArgs a) {
       for (int d = 0; d < ND; ++d)
         dqacc[d] = mx_mma(mx_frag(sb + Sh::OFF_KT + (d * 32 + l32) * Tl::TPITCH, g), sop, dqacc[d],
                           scale_byte(g ? kw[1] : kw[0], d), ssc);
-      stage ^= 1;
+      stage = stage + 1 == NS ? 0 : stage + 1;
+    };
+    if (n > 0) {
+      for (int t = 0; t + 1 < n; ++t) step(std::false_type{}, t);
+      step(std::true_type{}, n - 1);
     }
-    if (q < s.lq) {
-      TG* dqrow = reinterpret_cast<TG*>(a.dq) + ((int64_t)(s.q0 + q) * H + h) * D;
+    {
+      const rsrc_t rq = make_rsrc(reinterpret_cast<const TG*>(a.dq) + ((int64_t)x.s.q0 * H + x.h) * D,
+                                  (uint32_t)x.s.lq * HD * (uint32_t)sizeof(TG));
+      const uint32_t vrow = q < x.s.lq ? (uint32_t)(q * HD) * (uint32_t)sizeof(TG) : 0x80000000u;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          store4<TG>(dqrow + d * 32 + i4 * 8 + g * 4, a.scale * dqacc[d][i4 * 4], a.scale * dqacc[d][i4 * 4 + 1],
-                     a.scale * dqacc[d][i4 * 4 + 2], a.scale * dqacc[d][i4 * 4 + 3]);
+          buf_store4<TG>(rq, vrow + (uint32_t)(d * 32 + i4 * 8 + g * 4) * (uint32_t)sizeof(TG),
+                         a.scale * dqacc[d][i4 * 4], a.scale * dqacc[d][i4 * 4 + 1], a.scale * dqacc[d][i4 * 4 + 2],
+                         a.scale * dqacc[d][i4 * 4 + 3]);
+      ring.counted(ND * 4);
     }
   }
+  // every production was acquired; only stores can still be in flight
+  wait_vmcnt<0>();
 }
 
 }  // namespace jattn

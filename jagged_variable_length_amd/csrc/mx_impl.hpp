@@ -30,6 +30,7 @@
 #include "fwd_impl.hpp"
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
+#include "ring.hpp"
 
 namespace jattn {
 
@@ -156,7 +157,9 @@ __global__ __launch_bounds__(2 * D) void mx_quant_kernel(MxQuantArgs a) {
 //                    rescale; P scaled by 2^-Xp, Xp from the step's row max
 //   O^T += V^T P^T   A = V^T (LDS, codes_t), B = P after lane exchanges
 // K rows and V^T come HBM -> LDS through buffer loads whose destination is
-// LDS, two stages deep, one barrier per step.  Keys past the sample end read
+// LDS, into a ring of up to four stages filled by a producer cursor that
+// runs ahead across unit boundaries (each step waits only for its own
+// loads, with per-wave counts), one barrier per step.  Keys past the sample end read
 // as zeros in both tiles (K rows past the descriptor end; codes_t tokens past
 // the sample end are zero or past the descriptor end), so the padding
 // subtraction of the bf16 kernels applies unchanged.
@@ -171,8 +174,11 @@ struct MxFwdShape {
   static constexpr int V_NI = (D * V_SPR + 63) / 64;
   static constexpr int V_BYTES = V_NI * 1024;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int SMEM = 2 * STAGE;
-  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  static constexpr int NS = NS_FIT >= 4 ? 4 : NS_FIT;
+  static_assert(NS >= 2, "two stages at least");
+  static constexpr int SMEM = NS * STAGE;
+  static constexpr int KNI = KT::template ninst<BN>();  // LDS-destination loads of one step
 };
 
 // Plan records through scalar loads (wave-uniform addresses, read-only data).
@@ -202,15 +208,17 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int worker = xcd_worker(blockIdx.x, gridDim.x);
-  const int u_begin = uniform(a.worker_off[worker]);
-  const int u_end = uniform(a.worker_off[worker + 1]);
+  const int u_begin = sload1(a.worker_off, worker);
+  const int u_end = sload1(a.worker_off, worker + 1);
   const int H = a.H;
   const int HD = H * D;  // bytes per token row of codes
   const int64_t BLK = (int64_t)H * D * 32;  // bytes per row block of codes_t
+  constexpr int NS = Sh::NS;
   const uint32_t smem_lds = lds_addr(smem);
 
   RowLoader<D / 2, 1, BN, 4> kload;
   kload.init(wave, lane, HD / 2);
+  static_assert(decltype(kload)::NI == Sh::KNI, "the ring's per-step counts are the loaders' instruction counts");
   // V^T loader: slot s -> feature s/5, 16-byte chunk s%5 (chunk 4 = pad);
   // chunks 0,1 from the step's first token block, 2,3 from its second
   uint32_t vvoff[(Sh::V_NI + 3) / 4];
@@ -228,35 +236,17 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
   };
   auto fetch = [&](int u) {
     UnitInfo x;
-    const i32x4 un = load_unit(a.units, u);
+    const i32x4 un = sload4(a.units, u);
     x.b = un[0];
     x.h = un[1];
     x.qt = un[2];
     x.n = un[3];
-    x.s = load_sample(a.samples, x.b);
-    const i32x2 rb = reinterpret_cast<const i32x2*>(a.samples + 8 * x.b + 6)[0];
-    x.qblk0 = uniform(rb[0]);
-    x.kblk0 = uniform(rb[1]);
+    x.s = sload_sample(a.samples, x.b);
+    const i32x4 y = sload4(a.samples, 2 * x.b + 1);  // entries 4..7: bias0, row-block bases
+    x.qblk0 = y[2];
+    x.kblk0 = y[3];
     x.nkblk = (x.s.lk + 31) >> 5;
     return x;
-  };
-  auto issue_step = [&](const UnitInfo& x, int t, int st) {
-    const uint32_t sb = smem_lds + st * Sh::STAGE;
-    // K rows t*64 .. of (sample, head): zero past the sample end
-    const int64_t row0 = (int64_t)t * BN;
-    const i32x4 rk = rsrc_words(a.k.codes + ((int64_t)x.s.k0 * H + x.h) * D, 0);
-    kload.issue(sb, rsrc_at(rk, row0 * HD, (int64_t)(x.s.lk - t * BN) * HD), wave);
-    // V^T of token blocks kblk0 + 2t and + 2t + 1 (head h); the descriptor
-    // ends with the sample's last block, so a block past it reads zero
-    const int64_t vb = (int64_t)(x.kblk0 + 2 * t) * H + x.h;
-    const int64_t vend = ((int64_t)(x.kblk0 + x.nkblk - 1) * H + x.h + 1) * D * 32;
-    const i32x4 rv = rsrc_words(a.v.codes_t, 0);
-    const i32x4 rvs = rsrc_at(rv, vb * D * 32, vend - vb * D * 32);
-#pragma unroll
-    for (int j = 0; j < (Sh::V_NI + 3) / 4; ++j) {
-      const int inst = wave + 4 * j;
-      if (inst < Sh::V_NI) lds_dma16(rvs, sb + Sh::K_BYTES + inst * 1024, vvoff[j]);
-    }
   };
   // Q fragments (B operand) of this wave's 32 rows and their scale bytes
   auto load_q = [&](const UnitInfo& x, i32x8* qf, int* qsc) {
@@ -276,12 +266,67 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
   };
 
   if (u_begin >= u_end) return;
+
+  // ---- producer: the worker's steps in order, NS - 1 ahead of the consumer ----
+  // A step moves K rows 64t .. of (sample, head) (zero past the sample end)
+  // and V^T of token blocks kblk0 + 2t, + 2t + 1 (the descriptor ends with
+  // the sample's last block, so a block past it reads zero).  Descriptors
+  // are set up once per unit and advanced by a constant per step.
+  constexpr int LOOK = NS - 1;
+  constexpr int VJ = (Sh::V_NI + 3) / 4;
+  const int step_ops = loads_of(Sh::KNI, wave, 4) + loads_of(Sh::V_NI, wave, 4);
+  constexpr int MIN_OPS = loads_of(Sh::KNI, 3, 4) + loads_of(Sh::V_NI, 3, 4);
+  constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
+  VmLedger<LOOK, WAIT_N> ring;
+  int pu = u_begin, pt = 0, pn = 0, pst = 0;
+  Walker<false> w_k, w_v;
+  auto start_unit = [&](const UnitInfo& x) {
+    w_k.start(a.k.codes, ((int64_t)x.s.k0 * H + x.h) * D, (int64_t)x.s.lk * HD);
+    const int64_t vb = (int64_t)x.kblk0 * H + x.h;
+    const int64_t vend = ((int64_t)(x.kblk0 + x.nkblk - 1) * H + x.h + 1) * D * 32;
+    w_v.start(a.v.codes_t, vb * D * 32, vend - vb * D * 32);
+  };
+  UnitInfo pinfo = fetch(u_begin);
+  pn = pinfo.n;
+  if (pn > 0) start_unit(pinfo);
+  auto produce = [&]() {
+    if (pt >= pn && pu < u_end) {
+      do {
+        ++pu;
+        if (pu < u_end) pinfo = fetch(pu);
+      } while (pu < u_end && pinfo.n == 0);
+      pt = 0;
+      pn = pu < u_end ? pinfo.n : 0;
+      if (pn > 0) start_unit(pinfo);
+    }
+    if (pt < pn) {
+      const uint32_t sb = smem_lds + pst * Sh::STAGE;
+      kload.issue(sb, w_k.words(), wave);
+      const i32x4 rvs = w_v.words();
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) {
+        const int inst = wave + 4 * j;
+        if (inst < Sh::V_NI) lds_dma16(rvs, sb + Sh::K_BYTES + inst * 1024, vvoff[j]);
+      }
+      w_k.advance((int64_t)BN * HD);
+      w_v.advance(2 * BLK);
+      ++pt;
+      pst = pst + 1 == NS ? 0 : pst + 1;
+      ring.produced(step_ops);
+    } else {
+      ring.produced(0);
+    }
+  };
+
   UnitInfo cur = fetch(u_begin);
   i32x8 qf[NC];
   int qsc[NC];
   load_q(cur, qf, qsc);
+  // the first unit's Q has landed before anything else is issued (see the
+  // bf16 forward: later Q loads are followed by visible stores)
+  wait_vmcnt<0>();
+  for (int j = 0; j < LOOK; ++j) produce();
   int stage = 0;
-  if (cur.n > 0) issue_step(cur, 0, 0);
 
   for (int u = u_begin; u < u_end; ++u) {
     const bool has_next = u + 1 < u_end;
@@ -295,15 +340,16 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
     float m_run = 0.0f, l_run = 0.0f;
     bool pad_drop = false;
 
-    auto step = [&](auto first_tag, int t) {
+    // LAST (step n-1) alone loads the next unit's Q: the loop over the other
+    // steps then carries no register loads for the compiler to wait on
+    auto step = [&](auto first_tag, auto last_tag, int t) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      wait_vmcnt0();
-      __syncthreads();
-      if (t + 1 < n) {
-        issue_step(cur, t + 1, stage ^ 1);
-      } else if (has_next && nxt.n > 0) {
-        issue_step(nxt, 0, stage ^ 1);
-      }
+      constexpr bool LAST = decltype(last_tag)::value;
+      ring.wait_oldest();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // step t is in LDS; every wave is done with the stage produce() refills
+      __builtin_amdgcn_sched_barrier(0);
+      produce();
       const char* kt = smem + stage * Sh::STAGE;
       const char* vt = kt + Sh::K_BYTES;
       // scale words of the step's two key blocks (a block past the sample: any finite scale)
@@ -326,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
           sacc[kb] = mx_mma(mx_frag(krow + c * 64, g), qf[c], sacc[kb], scale_byte(ksw, 2 * c + g), qsc[c]);
       }
       // Q is dead after the last S^T of the unit: fetch the next unit's rows
-      if (t + 1 == n && has_next) load_q(nxt, qf, qsc);
+      if (LAST && has_next) load_q(nxt, qf, qsc);
 
       // slot (kb, i) of lane (query l32, g) holds key 64t + 32kb + acc_row(i, g)
       float p[2][16];
@@ -340,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
         // guard of the subtraction scheme (see the bf16 forward): a row whose
         // best valid score in the last step is below 0 drops the padded keys
         const int rem = cur.s.lk - t * BN;  // valid keys of this step
-        if (t + 1 == n && rem < BN) {
+        if (LAST && rem < BN) {
           float vm = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -430,11 +476,14 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
         oacc[d] = mx_mma(mx_frag(vt + (d * 32 + l32) * Sh::VPITCH, g), pb, oacc[d], scale_byte(g ? vsw1 : vsw0, d),
                          psc);
       }
-      stage ^= 1;
+      stage = stage + 1 == NS ? 0 : stage + 1;
     };
-    if (n > 0) {
-      step(std::true_type{}, 0);
-      for (int t = 1; t < n; ++t) step(std::false_type{}, t);
+    if (n == 1) {
+      step(std::true_type{}, std::true_type{}, 0);
+    } else if (n > 1) {
+      step(std::true_type{}, std::false_type{}, 0);
+      for (int t = 1; t + 1 < n; ++t) step(std::false_type{}, std::false_type{}, t);
+      step(std::false_type{}, std::true_type{}, n - 1);
     }
 
     // ---- epilogue ----
@@ -444,32 +493,44 @@ __global__ __launch_bounds__(256, 1) void mx_fwd_kernel(MxFwdArgs a) {
       if (n > 0 && !pad_drop) npad = n * BN - cur.s.lk;
       if (npad > 0) l_run -= (float)npad * fast_exp2(-m_run);
     }
+    // buffer stores issued by every lane (rows past the sample end at an
+    // out-of-range offset): the count the ring's waits rely on does not
+    // depend on the data, and the stores stay in flight across later waits
     const int qrow = cur.qt * BM + wave * 32 + l32;
-    if (qrow < cur.s.lq) {
-      TO* orow = reinterpret_cast<TO*>(a.o) + ((int64_t)(cur.s.q0 + qrow) * H + cur.h) * D;
+    const bool valid_row = qrow < cur.s.lq;
+    {
       const bool has_keys = cur.s.lk > 0;
       float inv = 1.0f;
       if constexpr (SOFTMAX) inv = has_keys ? 1.0f / l_run : 0.0f;
+      const rsrc_t ro = make_rsrc(reinterpret_cast<const TO*>(a.o) + ((int64_t)cur.s.q0 * H + cur.h) * D,
+                                  (uint32_t)cur.s.lq * HD * (uint32_t)sizeof(TO));
+      const uint32_t vrow = valid_row ? (uint32_t)(qrow * HD) * (uint32_t)sizeof(TO) : 0x80000000u;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          store4<TO>(orow + d * 32 + i4 * 8 + g * 4, oacc[d][i4 * 4] * inv, oacc[d][i4 * 4 + 1] * inv,
-                     oacc[d][i4 * 4 + 2] * inv, oacc[d][i4 * 4 + 3] * inv);
-      if (SOFTMAX && a.lse != nullptr && g == 0)
-        a.lse[((int64_t)cur.s.q0 + qrow) * H + cur.h] = has_keys ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+          buf_store4<TO>(ro, vrow + (uint32_t)(d * 32 + i4 * 8 + g * 4) * (uint32_t)sizeof(TO),
+                         oacc[d][i4 * 4] * inv, oacc[d][i4 * 4 + 1] * inv, oacc[d][i4 * 4 + 2] * inv,
+                         oacc[d][i4 * 4 + 3] * inv);
+      ring.counted(ND * 4);
+      if (SOFTMAX && a.lse != nullptr) {
+        const rsrc_t rl = make_rsrc(a.lse + (int64_t)cur.s.q0 * H + cur.h, (uint32_t)cur.s.lq * H * 4);
+        const float lse = has_keys ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl,
+                                              valid_row && g == 0 ? (uint32_t)qrow * H * 4 : 0x80000000u, 0, 0);
+        ring.counted(1);
+      }
     }
 
-    if (has_next) {
-      if (n == 0) load_q(nxt, qf, qsc);
-      if (n == 0 && nxt.n > 0) {
-        wait_vmcnt0();
-        __syncthreads();
-        issue_step(nxt, 0, stage);
-      }
+    if (has_next && n == 0) {
+      // a unit without keys did not load the next Q (rare: wait here)
+      load_q(nxt, qf, qsc);
+      wait_vmcnt<0>();
     }
     cur = nxt;
   }
+  // every production was acquired; only stores can still be in flight
+  wait_vmcnt<0>();
 }
 
 }  // namespace jattn
