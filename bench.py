@@ -66,6 +66,14 @@ def copy_calibration(mib, steps):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
+def rowstats_in_dq(w):
+    """Whether the library's dQ pass forms Di and LSE*log2e itself (bf16
+    softmax without the block mask, except D = 128 with fp32 O): then
+    there is no separate Di pass, and dQ runs before dK/dV."""
+    return (w.act == "softmax" and not w.block_diagonal and not w.mxfp8 and w.dtype == "bf16"
+            and not (w.D == 128 and w.out_dtype == "f32"))
+
+
 def kernel_work(w, info, es_in, es_out, es_g, es_db=4, mx=None):
     """Algorithmic bytes and FLOPs of each launch (every interface tensor once)."""
     H, D = w.H, w.D
@@ -98,7 +106,11 @@ def kernel_work(w, info, es_in, es_out, es_g, es_db=4, mx=None):
                  + 2 * kd * es_g + dbias_out, 2.0 * F),
         "dq": (2 * qd * es_in + 2 * kd * es_in + bias_in + (2 * rowstat if soft else 0) + qd * es_g, 0.5 * F),
     }
-    if soft:
+    if soft and rowstats_in_dq(w):
+        # dQ also reads O and LSE and writes Di and LSE*log2e (instead of reading them)
+        b_, f_ = work["dq"]
+        work["dq"] = (b_ + qd * es_out + rowstat, f_ + 2.0 * qd)
+    elif soft:
         work["prep"] = (qd * es_out + qd * es_in + rowstat, 2.0 * qd)
     if w.qk_norm:
         # read Q and K, write their normalised copies and 1/||row||; the
@@ -579,9 +591,13 @@ def main():
             A.qk_norm_backward(dev["k"], dk_att, out=dk)
         launches = [("qknorm", qknorm)] if w.qk_norm else []
         launches.append(("fwd", fwd))
-        if w.act == "softmax":
-            launches.append(("prep", stage(Bd.JATTN_BWD_PREP)))
-        launches += [("dkdv", stage(Bd.JATTN_BWD_DKDV)), ("dq", stage(Bd.JATTN_BWD_DQ))]
+        if rowstats_in_dq(w):
+            # the order jattn_bwd runs: dQ (forming Di and LSE*log2e), then dK/dV
+            launches += [("dq", stage(Bd.JATTN_BWD_DQ)), ("dkdv", stage(Bd.JATTN_BWD_DKDV))]
+        else:
+            if w.act == "softmax":
+                launches.append(("prep", stage(Bd.JATTN_BWD_PREP)))
+            launches += [("dkdv", stage(Bd.JATTN_BWD_DKDV)), ("dq", stage(Bd.JATTN_BWD_DQ))]
         if w.qk_norm:
             launches.append(("qknorm_bwd", qknorm_bwd))
 

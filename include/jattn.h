@@ -47,11 +47,9 @@
  *
  * Sharing one workspace.  The workspace holds the uploaded plan, which every
  * call only reads, and a scratch region (row statistics Di and LSE * log2 e)
- * that the backward's PREP stage writes and its DKDV and DQ stages read.
- * Forwards may therefore run concurrently on one workspace; DKDV and DQ may
- * run concurrently with each other (jattn_bwd_stages) once PREP is done; a
- * call that runs PREP (every jattn_bwd of a softmax plan without the block
- * mask) must not overlap another backward on the same workspace.
+ * that the backward writes and reads (see the stages below).  Forwards may
+ * therefore run concurrently on one workspace; a softmax backward (mask NONE
+ * or WINDOW) must not overlap another backward on the same workspace.
  *
  * Errors.  Every call returns JATTN_OK (0) or a negative JATTN_E_* code.
  * Arguments are validated on the host before anything is enqueued; on
@@ -231,10 +229,15 @@ int jattn_bwd(const jattn_plan* plan, const void* q, const void* k, const void* 
 #define JATTN_BWD_DQ 4   /* dQ */
 #define JATTN_BWD_ALL 7
 
-/* Same as jattn_bwd but runs only the stages in `stages`.  PREP must have
- * completed (on this or an ordered stream) before DKDV or DQ run; DKDV and
- * DQ are independent of each other and may run concurrently on two streams
- * (they write disjoint outputs and only read the workspace).  Block mode has
+/* Same as jattn_bwd but runs only the stages in `stages`, on one stream.
+ * Softmax plans (mask NONE or WINDOW) keep row statistics in the workspace:
+ * DKDV reads Di and LSE * log2 e, which PREP writes.  With bf16 inputs (except
+ * D = 128 with fp32 O) the DQ stage forms them itself from O, dO and LSE and
+ * writes them too: a call with DQ then skips PREP and runs DQ before DKDV,
+ * and DQ alone needs no earlier PREP.  Otherwise (fp32 inputs, or D = 128
+ * with fp32 O) DQ and DKDV both read them, and PREP must have completed (in
+ * this call or an earlier one on an ordered stream) before either.  DKDV
+ * run alone needs an earlier PREP or DQ of the same inputs.  Block mode has
  * a single fused stage, run when DKDV or DQ is requested. */
 int jattn_bwd_stages(const jattn_plan* plan, int32_t stages, const void* q, const void* k,
                      const void* v, const void* bias, const void* o, const float* lse,

@@ -546,7 +546,14 @@ int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, c
     if (e != hipSuccess) return hip_fail(e, "block backward launch");
     return ok();
   }
-  if (softmax_dense && p->Tq > 0 && (stages & JATTN_BWD_PREP)) {
+  // bf16 softmax: the dQ pass forms Di and LSE*log2e itself from O, dO and
+  // LSE and writes them for dK/dV, which then runs after it (not with fp32 O
+  // at D = 128, whose registers do not fit beside dQ's other operands)
+  const bool fold = softmax_dense && !sel.in_f32 && !(p->D == 128 && p->desc.out_dtype == JATTN_F32);
+  sel.o_f32 = p->desc.out_dtype == JATTN_F32;
+  sel.fold = fold;
+  const bool dq_forms_rowstats = fold && (stages & JATTN_BWD_DQ);
+  if (softmax_dense && p->Tq > 0 && (stages & JATTN_BWD_PREP) && !dq_forms_rowstats) {
     jattn::DiArgs da{o, dout, di, p->Tq * p->H, lse, lse2};
     e = jattn::launch_di(da, sel, p->desc.out_dtype == JATTN_F32, st);
     if (e != hipSuccess) return hip_fail(e, "Di launch");
@@ -571,18 +578,34 @@ int bwd_run(const jattn_plan* p, int32_t stages, const void* q, const void* k, c
   a.bias_elems = p->bias_elems;
   a.win_l = p->win_l;
   a.win_r = p->win_r;
-  if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
-    a.units = ws_ptr(workspace, p->off_dkdv_u);
-    a.worker_off = ws_ptr(workspace, p->off_dkdv_o);
-    e = jattn::launch_dkdv(a, sel, p->dkdv.num_workers, st);
-    if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  a.o = o;
+  if (fold) {
+    a.rs_di = di;
+    a.rs_lse2 = lse2;
   }
-  if (p->dq.n_units() > 0 && (stages & JATTN_BWD_DQ)) {
-    a.units = ws_ptr(workspace, p->off_dq_u);
-    a.worker_off = ws_ptr(workspace, p->off_dq_o);
-    e = jattn::launch_dq(a, sel, p->dq.num_workers, st);
-    if (e != hipSuccess) return hip_fail(e, "dQ launch");
-  }
+  auto run_dkdv = [&]() -> int {
+    if (p->dkdv.n_units() > 0 && (stages & JATTN_BWD_DKDV)) {
+      a.units = ws_ptr(workspace, p->off_dkdv_u);
+      a.worker_off = ws_ptr(workspace, p->off_dkdv_o);
+      const hipError_t e2 = jattn::launch_dkdv(a, sel, p->dkdv.num_workers, st);
+      if (e2 != hipSuccess) return hip_fail(e2, "dK/dV launch");
+    }
+    return JATTN_OK;
+  };
+  auto run_dq = [&]() -> int {
+    if (p->dq.n_units() > 0 && (stages & JATTN_BWD_DQ)) {
+      a.units = ws_ptr(workspace, p->off_dq_u);
+      a.worker_off = ws_ptr(workspace, p->off_dq_o);
+      const hipError_t e2 = jattn::launch_dq(a, sel, p->dq.num_workers, st);
+      if (e2 != hipSuccess) return hip_fail(e2, "dQ launch");
+    }
+    return JATTN_OK;
+  };
+  // with the row statistics formed by dQ, dK/dV reads them after it
+  const int r1 = fold ? run_dq() : run_dkdv();
+  if (r1 != JATTN_OK) return r1;
+  const int r2 = fold ? run_dkdv() : run_dq();
+  if (r2 != JATTN_OK) return r2;
   return ok();
 }
 

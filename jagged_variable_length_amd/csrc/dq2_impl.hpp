@@ -72,11 +72,16 @@ struct Dq2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
+// OF (softmax only): 0 = Di and LSE*log2e read from the workspace; 1 / 2 =
+// formed here from O (bf16 / fp32), dO and the natural LSE, and written to
+// the workspace for the dK/dV pass, which then runs after this one.
+template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false, int OF = 0>
 __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
   using Sh = Dq2Shape<D, WQ, WK, BIAS>;
   constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW, NS = Sh::NS;
   constexpr bool SOFTMAX = (ACT == kSoftmax);
+  constexpr bool FOLD = SOFTMAX && OF != 0;
+  static_assert(OF == 0 || SOFTMAX, "row statistics belong to softmax");
 
   __shared__ __attribute__((aligned(1024))) char smem[Sh::SMEM];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -135,6 +140,9 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(row * HD + kk * 16 + g * 8) * 2));
   };
+  // O of this lane's row in the dO layout (FOLD: bf16 or fp32 elements)
+  bf16x8 o16[OF == 1 ? NKK : 1];
+  f32x4 o32[OF == 2 ? 2 * NKK : 1];
   auto load_do = [&](const UnitInfo& x, bf16x8* dof, float& lse2, float& di) {
     const int64_t qo = ((int64_t)x.s.q0 * a.H + x.h) * D;
     const rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qo, (uint32_t)x.s.lq * HD * 2);
@@ -145,10 +153,28 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
     if constexpr (SOFTMAX) {
       // rows past the sample end read as zero, which keeps their terms finite
       const uint32_t rec = (uint32_t)x.s.lq * a.H * 4;
-      const rsrc_t rl = make_rsrc(a.lse2 + (int64_t)x.s.q0 * a.H + x.h, rec);
-      const rsrc_t rd = make_rsrc(a.di + (int64_t)x.s.q0 * a.H + x.h, rec);
-      lse2 = __uint_as_float(buf_load4(rl, (uint32_t)row * a.H * 4));
-      di = __uint_as_float(buf_load4(rd, (uint32_t)row * a.H * 4));
+      if constexpr (FOLD) {
+        // O and the natural LSE; Di and LSE*log2e are formed at the unit's start
+        if constexpr (OF == 1) {
+          const rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(a.o) + qo, (uint32_t)x.s.lq * HD * 2);
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            o16[kk] = __builtin_bit_cast(bf16x8, buf_load16(ro, (uint32_t)(row * HD + kk * 16 + g * 8) * 2));
+        } else {
+          const rsrc_t ro = make_rsrc(reinterpret_cast<const float*>(a.o) + qo, (uint32_t)x.s.lq * HD * 4);
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            o32[2 * kk] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)(row * HD + kk * 16 + g * 8) * 4));
+            o32[2 * kk + 1] = __builtin_bit_cast(f32x4, buf_load16(ro, (uint32_t)(row * HD + kk * 16 + g * 8 + 4) * 4));
+          }
+        }
+        lse2 = __uint_as_float(buf_load4(make_rsrc(a.lse + (int64_t)x.s.q0 * a.H + x.h, rec), (uint32_t)row * a.H * 4));
+      } else {
+        const rsrc_t rl = make_rsrc(a.lse2 + (int64_t)x.s.q0 * a.H + x.h, rec);
+        const rsrc_t rd = make_rsrc(a.di + (int64_t)x.s.q0 * a.H + x.h, rec);
+        lse2 = __uint_as_float(buf_load4(rl, (uint32_t)row * a.H * 4));
+        di = __uint_as_float(buf_load4(rd, (uint32_t)row * a.H * 4));
+      }
     }
   };
 
@@ -230,8 +256,38 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
     UnitInfo nxt = cur;
     if (has_next) nxt = fetch(u + 1);
     const int n = cur.n;
-    // row statistics of this unit (the next unit's are loaded during its last step)
-    const float lse2_u = lse2, di_u = di;
+    // row statistics of this unit (the next unit's rows are loaded during its last step)
+    float lse2_u = lse2, di_u = di;
+    if constexpr (FOLD) {
+      // Di = rowsum(dO * O) (each lane half holds half of the row) and
+      // LSE * log2(e), written for the dK/dV pass by the waves of key block 0
+      // (buffer stores from every lane, counted like the dQ stores)
+      float part = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (OF == 1) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            part = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{dof[kk][2 * j], dof[kk][2 * j + 1]},
+                                                   bf16x2{o16[kk][2 * j], o16[kk][2 * j + 1]}, part, false);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part = fmaf((float)dof[kk][j], o32[2 * kk + j / 4][j % 4], part);
+        }
+      }
+      di_u = wave_xor32_sum(part);
+      lse2_u = lse2 * kLog2e;
+      if (wk == 0) {
+        const int row = cur.qt * BM + wq * 32 + l32;
+        const uint32_t rec = (uint32_t)cur.s.lq * a.H * 4;
+        const uint32_t voff = row < cur.s.lq && g == 0 ? (uint32_t)row * a.H * 4 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(di_u), make_rsrc(a.rs_di + (int64_t)cur.s.q0 * a.H + cur.h, rec),
+                                              voff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2_u),
+                                              make_rsrc(a.rs_lse2 + (int64_t)cur.s.q0 * a.H + cur.h, rec), voff, 0, 0);
+        ring.counted(2);
+      }
+    }
 
     f32x16 dqacc[ND];
 #pragma unroll

@@ -12,18 +12,37 @@ typedef float f32;
 
 namespace {
 
-template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
-hipError_t dq2_one(const BwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((dq2_kernel<J_TG, J_D, WQ, WK, ACT, BIAS, SPLIT, WIN>), dim3(grid), dim3(64 * WQ * WK), 0,
+template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false, int OF = 0>
+hipError_t dq2_launch(const BwdArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((dq2_kernel<J_TG, J_D, WQ, WK, ACT, BIAS, SPLIT, WIN, OF>), dim3(grid), dim3(64 * WQ * WK), 0,
                      st, a);
   return hipGetLastError();
+}
+// softmax: dQ forms Di and LSE * log2(e) itself (k.fold) from bf16 O, or from
+// fp32 O below D = 128; at D = 128 fp32 O does not fit the registers beside
+// the unit's other operands, and those plans keep the separate Di pass
+template <int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
+hipError_t dq2_one(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
+  if constexpr (ACT == kSoftmax) {
+    if (!k.fold) {
+      if constexpr (J_D == 128) return dq2_launch<WQ, WK, ACT, BIAS, SPLIT, WIN, 0>(a, grid, st);
+      return hipErrorInvalidValue;
+    }
+    if (k.o_f32) {
+      if constexpr (J_D < 128) return dq2_launch<WQ, WK, ACT, BIAS, SPLIT, WIN, 2>(a, grid, st);
+      return hipErrorInvalidValue;
+    }
+    return dq2_launch<WQ, WK, ACT, BIAS, SPLIT, WIN, 1>(a, grid, st);
+  } else {
+    return dq2_launch<WQ, WK, ACT, BIAS, SPLIT, WIN>(a, grid, st);
+  }
 }
 // sliding window: 128-row query tiles, 64-key steps only
 template <int ACT>
 hipError_t dq2_window(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.wq != 4) return hipErrorInvalidValue;
-  if (k.bias) return k.split ? dq2_one<4, 2, ACT, true, true, true>(a, grid, st) : dq2_one<4, 2, ACT, true, false, true>(a, grid, st);
-  return k.split ? dq2_one<4, 2, ACT, false, true, true>(a, grid, st) : dq2_one<4, 2, ACT, false, false, true>(a, grid, st);
+  if (k.bias) return k.split ? dq2_one<4, 2, ACT, true, true, true>(a, k, grid, st) : dq2_one<4, 2, ACT, true, false, true>(a, k, grid, st);
+  return k.split ? dq2_one<4, 2, ACT, false, true, true>(a, k, grid, st) : dq2_one<4, 2, ACT, false, false, true>(a, k, grid, st);
 }
 
 template <int WQ, int WK, int ACT>
@@ -32,11 +51,11 @@ hipError_t dq2_act(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t s
     // a 128-key step leaves no room for a bias tile at this head dim
     if (k.bias) return hipErrorInvalidValue;
   } else if (k.bias) {
-    if (k.split) return dq2_one<WQ, WK, ACT, true, true>(a, grid, st);
-    return dq2_one<WQ, WK, ACT, true, false>(a, grid, st);
+    if (k.split) return dq2_one<WQ, WK, ACT, true, true>(a, k, grid, st);
+    return dq2_one<WQ, WK, ACT, true, false>(a, k, grid, st);
   }
-  if (k.split) return dq2_one<WQ, WK, ACT, false, true>(a, grid, st);
-  return dq2_one<WQ, WK, ACT, false, false>(a, grid, st);
+  if (k.split) return dq2_one<WQ, WK, ACT, false, true>(a, k, grid, st);
+  return dq2_one<WQ, WK, ACT, false, false>(a, k, grid, st);
 }
 
 template <int WQ, int WK>

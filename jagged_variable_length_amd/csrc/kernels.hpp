@@ -62,6 +62,11 @@ struct BwdArgs {
   int64_t bias_elems;  // elements of the whole bias tensor (bounds its loads)
   int win_l, win_r;    // sliding window: query i sees keys i - win_l .. i + win_r
   const double* rope_theta;  // block mode with RoPE: theta_j, j < D/2 (else null)
+  // dQ with the row statistics folded in (bf16 softmax): O (out dtype) and the
+  // natural LSE are read, Di and LSE * log2(e) written here for dK/dV
+  const void* o;
+  float* rs_di;
+  float* rs_lse2;
 };
 
 // MXFP8 tensor as the kernels see it (see mx_impl.hpp for the layout)
@@ -132,6 +137,8 @@ struct KernelSel {
   int wq;         // fwd/dq: waves along queries (4 or 1; 1 => 4-way key split)
   int wkv;        // dkdv: waves along keys (4, 2 or 1; the rest split queries)
   bool window;    // sliding-window mask (bf16 inputs; wq = 4, wkv = 4)
+  bool o_f32;     // bwd, softmax: O is fp32 (else bf16)
+  bool fold;      // bwd, bf16 softmax: dQ forms Di and LSE*log2e (and runs before dK/dV)
 };
 
 #define JATTN_FWD_LAUNCHER_(D, TI, TO) launch_fwd_##D##_##TI##_##TO
