@@ -446,11 +446,12 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
           const char* kn = stage_k(next_stage(stage));
           f32x16 snx = f32x16{};
           bf16x8 ka[NKK];
-          ka[0] = rows_frag<D, 1>(kn, kb + l32, 0, g);
-          if constexpr (NKK > 1) ka[1] = rows_frag<D, 1>(kn, kb + l32, 1, g);
+          constexpr int KA = NKK < 4 ? NKK : 4;  // K fragments in flight
+#pragma unroll
+          for (int c = 0; c < KA; ++c) ka[c] = rows_frag<D, 1>(kn, kb + l32, c, g);
           auto mm = [&](int c) {
             snx = Elem<bf16>::mma(ka[c], qf[c], snx);
-            if (c + 2 < NKK) ka[c + 2] = rows_frag<D, 1>(kn, kb + l32, c + 2, g);
+            if (c + KA < NKK) ka[c + KA] = rows_frag<D, 1>(kn, kb + l32, c + KA, g);
           };
           soft(first_tag, last_tag, t, stage, sacc, mm, pf, pl);
           sacc = snx;
