@@ -370,19 +370,25 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const Window w{A_win_l, A_win_r, x.s.lq, x.s.lk};
     return w.full(step_row0(x, t) + wq * 32, x.kt * KT + wv * 32);
   };
+  // bias[q][key] of this lane's key column for its 16 accumulator rows (keys
+  // past lk carry the next row's values; only their own, unstored columns see
+  // them): the rows of slots 8s .. 8s+7 are the ones a transposed read of
+  // step s delivers to the lane (two ds_read_b64_tr_b16 each), in slot order
+  auto bias_frag = [&](const char* stage_base, float* out) __attribute__((always_inline)) {
+    const char* bt = stage_base + Sh::OFF_B;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 v = trans_frag<KT, 1>(bt, wq, s2, wv * 32, lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[s2 * 8 + j] = (float)v[j];
+    }
+  };
   auto softmax = [&](const Unit& x, int t, int st, const SD& sd) __attribute__((always_inline)) {
     const f32x16 sacc = sd.s, dpacc = sd.dp;
     Ops o;
     const char* qt = smem + st * Sh::STAGE;
     float p[16], ds[16];
-    if constexpr (BIAS) {
-      // bias[q][key] for the 16 query rows of this lane (keys past lk carry
-      // the next row's values; only their own, unstored columns see them)
-      const char* bt = qt + Sh::OFF_B + (wq * 32 + g * 4) * Sh::BT::PITCH + (wv * 32 + l32) * 2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        p[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(bt + acc_row(i, 0) * Sh::BT::PITCH) << 16);
-    }
+    if constexpr (BIAS) bias_frag(qt, p);
     if constexpr (SOFTMAX) {
       const char* rs = qt + Sh::OFF_RS;
       constexpr int DI_OFF = (Sh::NRS / 2) * 256;
@@ -489,12 +495,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const char* on = qn + Sh::OFF_O;
     const char* qt = smem + cs_ * Sh::STAGE;
     float bias[16], lse[16], di[16];
-    if constexpr (BIAS) {
-      const char* bt = qt + Sh::OFF_B + (wq * 32 + g * 4) * Sh::BT::PITCH + (wv * 32 + l32) * 2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        bias[i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(bt + acc_row(i, 0) * Sh::BT::PITCH) << 16);
-    }
+    if constexpr (BIAS) bias_frag(qt, bias);
     if constexpr (SOFTMAX) {
       const char* rs = qt + Sh::OFF_RS;
       constexpr int DI_OFF = (Sh::NRS / 2) * 256;
