@@ -32,6 +32,9 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+WARM_S = 0.5  # seconds of back-to-back untimed steps before the timed region
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,10 +604,17 @@ def main():
         if w.qk_norm:
             launches.append(("qknorm_bwd", qknorm_bwd))
 
-    for _ in range(args.warmup):
-        for _, f in launches:
-            f()
-    torch.cuda.synchronize()
+    # Warm-up: the W steps asked for, then more (untimed) until the GPU has run
+    # steps back to back for WARM_S seconds: after any pause the first steps run
+    # slower (clock and caches ramping up), and the timed steps that follow
+    # without a host pause should see the steady state.
+    warm_steps, t_warm = 0, time.perf_counter()
+    while warm_steps < args.warmup or time.perf_counter() - t_warm < WARM_S:
+        for _ in range(4):
+            for _, f in launches:
+                f()
+            warm_steps += 1
+        torch.cuda.synchronize()
 
     ev = {n: [] for n, _ in launches}
     step_ev = []
@@ -683,6 +693,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_events": {"median": round(float(np.median(step_ms)), 4), "min": round(float(np.min(step_ms)), 4),
                                "mean": round(float(np.mean(step_ms)), 4)},
