@@ -46,6 +46,8 @@ def units():
             u.append(("dq2_inst.hip", f"dq2_{d}_{tg}", [f"-DJ_D={d}", f"-DJ_TG={tg}"]))
         u.append(("bwd_inst.hip", f"di_{d}_bf16", [f"-DJ_D={d}", "-DJ_TI=bf16", "-DJ_TG=bf16", "-DJ_DI",
                                                    "-DJ_DI_ONLY"]))
+    for tg in ("bf16", "f32"):
+        u.append(("bwd_pair_inst.hip", f"dkdv_pair_128_{tg}", ["-DJ_D=128", f"-DJ_TG={tg}"]))
     for d in (128, 64):
         u.append(("mx_inst.hip", f"mx_{d}", [f"-DJ_D={d}"]))
     for d in F32_DIMS:
