@@ -50,7 +50,11 @@ struct DkdvPairShape {
   static constexpr int KB = 4;   // 32-key blocks per unit
   static constexpr int KT = 32 * KB;
   static constexpr int QS = 32;  // queries per step
-  static constexpr int PAD = 2;
+  // Q and dO rows with three spare 16-byte slots: the row pitch moves the
+  // 16-byte chunk of consecutive rows by 12 banks, so the 16 rows of a
+  // ds_read_b128 group fall on distinct banks, and the 4 rows of a
+  // transposed-read group on disjoint 8-bank spans
+  static constexpr int PAD = D == 128 ? 3 : 2;
   using QT = PadTile<D, PAD>;
   static constexpr int Q_BYTES = QT::template bytes<QS>();
   using BT = PadTile<KT, 1>;
