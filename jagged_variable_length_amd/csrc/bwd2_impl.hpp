@@ -173,7 +173,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       2 * loads_of(Sh::QNI, NW - 1, NW) + loads_of(Sh::NRS, NW - 1, NW) + loads_of(Sh::BNI, NW - 1, NW);
   constexpr int LOOK = NS - 2;  // productions in flight at an acquisition
   constexpr int WAIT_N = (LOOK - 1) * MIN_OPS < 63 ? (LOOK - 1) * MIN_OPS : 63;
-  VmLedger<LOOK, WAIT_N> ring;
+  // with dBias, the stores of LOOK steps are issued after the oldest
+  // production as well in the steady state
+  constexpr int WAIT_N2 = WAIT_N + LOOK * S_OPS < 63 ? WAIT_N + LOOK * S_OPS : 63;
+  VmLedger<LOOK, WAIT_N, WAIT_N2> ring;
 
   int pu = u_begin, pt = 0, pn = 0, pst = 0;
   Unit pinfo;

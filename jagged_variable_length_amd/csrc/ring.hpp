@@ -81,9 +81,12 @@ __device__ __forceinline__ constexpr int loads_of(int NI, int part, int NP) {
 // enough; when fewer follow (the last steps of the worker), vmcnt(0).  A
 // wave that issued more than N after it waits a little longer than needed.
 // One compare and branch instead of a dispatch over every possible count.
-template <int L, int N>
+// N2 > N adds a second level for waves that also count stores between
+// productions (N2 = N plus the stores of the steps in flight): without it
+// every wait would also wait for those stores.
+template <int L, int N, int N2 = 0>
 struct VmLedger {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static_assert(N >= 0 && N < 64 && N2 < 64, "vmcnt range");
   int issued = 0;
   int mark[L] = {};
   __device__ __forceinline__ void produced(int ops) {
@@ -96,10 +99,17 @@ struct VmLedger {
   __device__ __forceinline__ void counted(int ops) { issued += ops; }
   // wait until the loads of the oldest production in flight have landed
   __device__ __forceinline__ void wait_oldest() const {
+    const int after = issued - mark[L - 1];
+    if constexpr (N2 > N) {
+      if (after >= N2) {
+        wait_vmcnt<N2>();
+        return;
+      }
+    }
     if constexpr (N == 0) {
       wait_vmcnt<0>();
     } else {
-      if (issued - mark[L - 1] >= N)
+      if (after >= N)
         wait_vmcnt<N>();
       else
         wait_vmcnt<0>();
