@@ -272,9 +272,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   };
 
-  // S = Q K^T (P wave) or dP = dO V^T (dS wave) of the step in stage st
+  // dP = dO V^T of the step in stage st (dS wave)
   auto rows_mma = [&](int st) __attribute__((always_inline)) {
-    const char* t = smem + st * Sh::STAGE + (role == 0 ? 0 : Sh::OFF_O);
+    const char* t = smem + st * Sh::STAGE + Sh::OFF_O;
     // every operand read issued before the first MFMA of the chain
     bf16x8 fr[NKK];
 #pragma unroll
@@ -287,36 +287,59 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
   // acc[d] += X^T Y for the 32 rows of stage st's tile X (Q or dO), Y = the
   // packed bf16 operand (P or dS) of this lane's key column
+  // (every operand read issued before the first MFMA: left to the compiler
+  // at this register pressure, each MFMA waits for its own read)
   auto trans_mma = [&](const char* x, const bf16x8* y, f32x16* acc) __attribute__((always_inline)) {
+    bf16x8 xa[2][ND];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] = Elem<bf16>::mma(trans_frag<D, PAD>(x, 0, s2, d * 32, lane), y[s2], acc[d]);
+      for (int d = 0; d < ND; ++d) xa[s2][d] = trans_frag<D, PAD>(x, 0, s2, d * 32, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] = Elem<bf16>::mma(xa[s2][d], y[s2], acc[d]);
   };
   char* const px = smem + Sh::OFF_PX + wv * Sh::PREC + lane * 16;
 
-  // ---- P wave: P of step t (stage st) from S, hand-over, dV^T += dO^T P ----
-  auto p_tail = [&](int t, int st, const f32x16& s, f32x16* acc) __attribute__((always_inline)) {
+  // ---- P wave, step t (stage st): S = Q K^T, P, hand-over, dV^T += dO^T P.
+  // The LDS reads that S and P need are all issued while the S MFMAs run
+  // (left to the compiler, the row statistics and bias are read after them,
+  // each waited for on its own); with LOAD the next unit's K fragments load
+  // right after the S MFMAs, their last use ----
+  auto p_step = [&](auto load_tag, int u, int t, int st, f32x16* acc) __attribute__((always_inline)) {
+    constexpr bool LOAD = decltype(load_tag)::value;
     const char* qt = smem + st * Sh::STAGE;
-    float p[16];
+    bf16x8 fr[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) fr[kk] = rows_frag<D, PAD>(qt, l32, kk, g);
+    __builtin_amdgcn_sched_barrier(0);
+    // the row statistics and bias values are read once half of the S
+    // operands have been consumed (registers), ahead of the other half
+    constexpr int KH = NKK / 2;
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) sacc = Elem<bf16>::mma(fr[kk], kvf[kk], sacc);
+    f32x4 l4[4];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) l4[i4] = *reinterpret_cast<const f32x4*>(qt + Sh::OFF_RS + (i4 * 8 + g * 4) * 4);
+    // bias[q][key] of this lane's key column in accumulator row order
+    bf16x8 bv[2];
     if constexpr (BIAS) {
-      // bias[q][key] of this lane's key column in accumulator row order
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 v = trans_frag<KT, 1>(qt + Sh::OFF_B, 0, s2, wv * 32, lane);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[s2 * 8 + j] = (float)v[j];
-      }
+      for (int s2 = 0; s2 < 2; ++s2) bv[s2] = trans_frag<KT, 1>(qt + Sh::OFF_B, 0, s2, wv * 32, lane);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(qt + Sh::OFF_RS + (i4 * 8 + g * 4) * 4);
+    for (int kk = KH; kk < NKK; ++kk) sacc = Elem<bf16>::mma(fr[kk], kvf[kk], sacc);
+    if constexpr (LOAD) load_next_kv(u);
+    float p[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i4 * 4 + j;
-        const float c = BIAS ? fmaf(p[i], kLog2e, -l4[j]) : -l4[j];
-        p[i] = fast_exp2(fmaf(s[i], A_scale_log2, c));
-      }
+    for (int i = 0; i < 16; ++i) {
+      const float lse = l4[i / 4][i % 4];
+      const float c = BIAS ? fmaf((float)bv[i / 8][i % 8], kLog2e, -lse) : -lse;
+      p[i] = fast_exp2(fmaf(sacc[i], A_scale_log2, c));
     }
     char* rec = px + (t & 1) * Sh::KB * Sh::PREC;
 #pragma unroll
@@ -427,28 +450,23 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       produce();
       patch_tail(x, 0, cs);
       if (role == 0) {
-        f32x16 s = rows_mma(cs);
         if (x.n == 1) {
-          load_next_kv(u);
-          p_tail(0, cs, s, acc);
+          p_step(std::true_type{}, u, 0, cs, acc);
           cs = next_stage(cs);
         } else {
-          p_tail(0, cs, s, acc);
+          p_step(std::false_type{}, u, 0, cs, acc);
           cs = next_stage(cs);
           for (int t = 1; t + 1 < x.n; ++t) {
             acquire();
             produce();
             patch_tail(x, t, cs);
-            s = rows_mma(cs);
-            p_tail(t, cs, s, acc);
+            p_step(std::false_type{}, u, t, cs, acc);
             cs = next_stage(cs);
           }
           acquire();
           produce();
           patch_tail(x, x.n - 1, cs);
-          s = rows_mma(cs);
-          load_next_kv(u);
-          p_tail(x.n - 1, cs, s, acc);
+          p_step(std::true_type{}, u, x.n - 1, cs, acc);
           cs = next_stage(cs);
         }
         // the partner reads P of the unit's last step after this barrier
