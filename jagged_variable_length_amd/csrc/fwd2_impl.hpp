@@ -407,14 +407,22 @@ __global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
       }
     };
 
-    // O^T += V^T P^T from the V tile in stage st
+    // O^T += V^T P^T from the V tile in stage st (every V^T read issued
+    // before the first MFMA: left to the compiler at this register pressure,
+    // the second half of the MFMAs each waits for its own read)
     auto pv = [&](int st, const bf16x8* pf, const bf16x8* pl) {
       const char* vt = stage_v(st);
+      bf16x8 va[2][ND];
+#pragma unroll
+      for (int s8 = 0; s8 < 2; ++s8)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) va[s8][d] = trans_frag<D, 2>(vt, wk, s8, d * 32, lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s8 = 0; s8 < 2; ++s8) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const bf16x8 vf = trans_frag<D, 2>(vt, wk, s8, d * 32, lane);
+          const bf16x8 vf = va[s8][d];
           oacc[d] = Elem<bf16>::mma(vf, pf[s8], oacc[d]);
           // split operands matter for the activation path only: softmax
           // already normalises by the sum of the rounded P
