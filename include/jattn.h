@@ -134,7 +134,11 @@ typedef struct {
                              of the rounded P and does not need it; for dV /
                              dK sums over thousands of queries it does. */
   int32_t order;        /* JATTN_HEAVY_FIRST | JATTN_ZIGZAG | JATTN_LPT */
-  int32_t num_workers;  /* persistent workers per kernel; 0 = default */
+  int32_t num_workers;  /* persistent workers per kernel; 0 = default.  The
+                           bf16 dK/dV pass at D <= 64 without bias or window
+                           on 64- or 128-key tiles (not erf-GELU) runs two
+                           workgroups per CU and is planned over twice this
+                           number (jattn_plan_summary reports each pass's) */
   int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
   int32_t window_left;  /* JATTN_MASK_WINDOW: keys before the query it sees (>= 0) */
   int32_t window_right; /* JATTN_MASK_WINDOW: keys after the query it sees (>= 0);

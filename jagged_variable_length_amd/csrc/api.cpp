@@ -296,7 +296,13 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     win.right = p->win_r;
     jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd, win);
     jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq, win);
-    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, W, order, &p->dkdv, win);
+    // the bf16 dK/dV kernel runs two workgroups per CU at D <= 64 without a
+    // bias or window on 64- or 128-key units (not with erf-GELU): twice the
+    // workers (the kernel's dkdv2_waves_per_simd applies the same rule)
+    const bool dkdv_two = d.in_dtype == JATTN_BF16 && d.D <= 64 && !d.has_bias && d.mask != JATTN_MASK_WINDOW &&
+                          p->dkdv_wkv >= 2 && d.act != JATTN_GELU_ERF;
+    jattn::plan_units(jattn::kKindDkdv, lq, lk, d.H, dkdv_tile, dkdv_step, dkdv_two ? 2 * W : W, order, &p->dkdv,
+                      win);
   }
   append(p->image, p->fwd, &p->off_fwd_u, &p->off_fwd_o);
   append(p->image, p->dkdv, &p->off_dkdv_u, &p->off_dkdv_o);

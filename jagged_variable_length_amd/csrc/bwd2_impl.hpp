@@ -48,7 +48,7 @@
 
 namespace jattn {
 
-template <int D, int WKV, int WKQ, bool SOFTMAX, bool BIAS>
+template <int D, int WKV, int WKQ, bool SOFTMAX, bool BIAS, bool TWO_ = false>
 struct Dkdv2Shape {
   static constexpr int NW = WKV * WKQ;
   static constexpr int KT = 32 * WKV;  // keys per unit
@@ -69,7 +69,9 @@ struct Dkdv2Shape {
   // query-split partials of dK^T (then dV^T) are summed through the stage of
   // the unit's last step, which is free once every wave has computed it
   static constexpr int COMB = WKQ > 1 ? (WKQ - 1) * WKV * D * 32 * 4 : 0;
-  static constexpr int NS_FIT = 160 * 1024 / STAGE;
+  // two workgroups per CU (dkdv2_waves_per_simd): each within half the LDS
+  static constexpr bool TWO = TWO_;
+  static constexpr int NS_FIT = (TWO ? 80 : 160) * 1024 / STAGE;
   static constexpr int NS = NS_FIT >= 4 ? 4 : 3;
   static constexpr int SMEM = NS * STAGE;
   static constexpr int QNI = QT::template ninst<QS>();
@@ -79,8 +81,19 @@ struct Dkdv2Shape {
 };
 
 // DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
+// At D <= 64 without a bias tile or window, on 64- or 128-key units, the
+// registers leave room for two waves per SIMD (not with erf-GELU, whose
+// derivative needs more): two workgroups per CU, each within half the LDS
+// (three stages), and the plan deals the units over twice as many workers
+template <int D, bool BIAS, bool WIN, int WKV, int ACT>
+constexpr int dkdv2_waves_per_simd() {
+  return D <= 64 && !BIAS && !WIN && WKV >= 2 && ACT != kGelu ? 2 : 1;
+}
+
 template <typename TG, int D, int WKV, int WKQ, int ACT, bool BIAS, int DBIAS, bool SPLIT, bool WIN = false>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv2_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) __attribute__((
+    amdgpu_waves_per_eu(dkdv2_waves_per_simd<D, BIAS, WIN, WKV, ACT>(), dkdv2_waves_per_simd<D, BIAS, WIN, WKV, ACT>()))) void
+dkdv2_kernel(BwdArgs a) {
   static_assert(!WIN || DBIAS == 0, "no dBias with a window");
   // Argument fields as locals: the lambdas below capture by reference, and a
   // reference to the argument block itself would keep it in scratch memory.
@@ -102,7 +115,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int64_t A_bias_elems = a.bias_elems;
   const int A_win_l = a.win_l, A_win_r = a.win_r;
   constexpr bool SOFTMAX = (ACT == kSoftmax);
-  using Sh = Dkdv2Shape<D, WKV, WKQ, SOFTMAX, BIAS>;
+  using Sh = Dkdv2Shape<D, WKV, WKQ, SOFTMAX, BIAS, dkdv2_waves_per_simd<D, BIAS, WIN, WKV, ACT>() == 2>;
   constexpr int NW = Sh::NW, KT = Sh::KT, QS = Sh::QS, ND = D / 32, NKK = D / 16, NS = Sh::NS;
   constexpr int PAD = Sh::PAD;
   constexpr int ESB = DBIAS == 2 ? 4 : 2;  // dBias element size

@@ -239,8 +239,11 @@ def test_random_plans_match(lib, seed):
             for kind, which, kp in parts:
                 units = B.jattn_plan_export(p, which * 2).reshape(-1, 4)
                 offs = B.jattn_plan_export(p, which * 2 + 1)
-                ref_u, ref_o = P.plan(kind, lq.tolist(), lk.tolist(), 3, kp.tile_rows, kp.step_rows, W,
-                                      ["heavy_first", "zigzag", "lpt"][order])
+                # the plan's own worker count of the pass (dK/dV at D = 64 without a
+                # bias runs two workgroups per CU over twice the workers asked for)
+                assert kp.num_workers in (W, 2 * W)
+                ref_u, ref_o = P.plan(kind, lq.tolist(), lk.tolist(), 3, kp.tile_rows, kp.step_rows,
+                                      kp.num_workers, ["heavy_first", "zigzag", "lpt"][order])
                 np.testing.assert_array_equal(units, np.array(ref_u, np.int32).reshape(-1, 4))
                 np.testing.assert_array_equal(offs, np.array(ref_o, np.int32))
         finally:
