@@ -849,9 +849,9 @@ hipError_t launch_dkdv(const BwdArgs& a, const KernelSel& k, int grid, hipStream
     if (k.D == 64) return launch_dkdv_64_f32_f32(a, k, grid, st);
     return launch_dkdv_32_f32_f32(a, k, grid, st);
   }
-  // softmax over a dense mask with 128-key units at D = 128: two waves per
-  // key block (P and dV; dP, dS and dK), two waves per SIMD
-  if (k.D == 128 && k.act == JATTN_SOFTMAX && !k.window && !k.split && k.wkv == 4)
+  // softmax (dense mask or window) with 128-key units at D = 128: two waves
+  // per key block (P and dV; dP, dS and dK), two waves per SIMD
+  if (k.D == 128 && k.act == JATTN_SOFTMAX && !k.split && k.wkv == 4)
     return k.out_f32 ? launch_dkdv_pair_128_f32(a, k, grid, st) : launch_dkdv_pair_128_bf16(a, k, grid, st);
   if (k.out_f32) {
     if (k.D == 128) return launch_dkdv2_128_f32(a, k, grid, st);

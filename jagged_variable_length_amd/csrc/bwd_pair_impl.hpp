@@ -26,6 +26,10 @@
 // The dS wave's MFMAs for dP of step t are interleaved with its VALU work on
 // dS of step t - 1.
 //
+// Sliding window (WIN, section "BlockAttention"): a unit's steps start at the
+// first query block whose window reaches its keys; the P wave zeroes P
+// outside the window, which makes dS zero there as well (no dBias).
+//
 // Memory pipeline: the ring of the single-wave kernel (Q, dO, bias tile and
 // row statistics of a step loaded HBM -> LDS ahead of use, NS - 2 steps in
 // flight, exact per-wave vmcnt waits), with its loads dealt over the eight
@@ -76,9 +80,10 @@ struct DkdvPairShape {
 };
 
 // DBIAS: 0 = no dBias, 1 = bf16 dBias, 2 = fp32 dBias
-template <typename TG, int D, bool BIAS, int DBIAS>
+template <typename TG, int D, bool BIAS, int DBIAS, bool WIN = false>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_pair_kernel(BwdArgs a) {
   static_assert(BIAS || DBIAS == 0, "dBias needs a bias");
+  static_assert(!WIN || DBIAS == 0, "no dBias with a window");
   const void* const A_q = a.q;
   const void* const A_k = a.k;
   const void* const A_v = a.v;
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const float A_scale = a.scale;
   const float A_scale_log2 = a.scale_log2;
   const int64_t A_bias_elems = a.bias_elems;
+  const int A_win_l = a.win_l, A_win_r = a.win_r;
   using Sh = DkdvPairShape<D, BIAS>;
   constexpr int NW = Sh::NW, KT = Sh::KT, QS = Sh::QS, ND = D / 32, NKK = D / 16, NS = Sh::NS;
   constexpr int PAD = Sh::PAD;
@@ -155,19 +161,25 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   Walker<true> w_b;
   int brows = 0;
   int64_t bstep = 0;
+  // first query row of step t (a windowed unit starts at the first query
+  // block whose window reaches its keys; the plan counts only those steps)
+  auto step_row0 = [&](const Unit& x, int t) __attribute__((always_inline)) {
+    return ((WIN ? window_first_step(x.kt * KT, A_win_r, QS) : 0) + t) * QS;
+  };
   auto start_unit = [&](const Unit& x) __attribute__((always_inline)) {
-    const int64_t qo = ((int64_t)x.s.q0 * H + x.h) * D * 2;
-    const int64_t rec = (int64_t)x.s.lq * HD * 2;
+    const int r0 = step_row0(x, 0);
+    const int64_t qo = ((int64_t)(x.s.q0 + r0) * H + x.h) * D * 2;
+    const int64_t rec = (int64_t)(x.s.lq - r0) * HD * 2;
     w_q.start(A_q, qo, rec);
     w_do.start(A_dout, qo, rec);
     // wave 0 loads LSE*log2e rows, wave 1 Di rows
-    w_rs.start(wave == 0 ? A_lse2 : A_di, ((int64_t)x.s.q0 * H + x.h) * 4, (int64_t)x.s.lq * H * 4);
+    w_rs.start(wave == 0 ? A_lse2 : A_di, ((int64_t)(x.s.q0 + r0) * H + x.h) * 4, (int64_t)(x.s.lq - r0) * H * 4);
     if constexpr (BIAS) {
       bload.init(wave, lane, x.s.lk);
       const int64_t e0 = x.s.bias0 + (int64_t)x.h * x.s.lq * x.s.lk;
-      const int64_t off = (int64_t)x.kt * KT * 2;
+      const int64_t off = ((int64_t)r0 * x.s.lk + (int64_t)x.kt * KT) * 2;
       w_b.start(reinterpret_cast<const char*>(A_bias) + e0 * 2, off, (A_bias_elems - e0) * 2 - off);
-      brows = x.s.lq;
+      brows = x.s.lq - r0;
       bstep = (int64_t)QS * x.s.lk * 2;
     }
   };
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           const rsrc_t rl = make_rsrc(reinterpret_cast<const bf16*>(A_bias) + (A_bias_elems - 1), 2);
           const uint16_t last = buf_load2(rl, 0);
           char* bt = smem + st * Sh::STAGE + Sh::OFF_B;
-          *reinterpret_cast<uint16_t*>(bt + ((x.s.lq - 1) - t * QS) * Sh::BT::PITCH +
+          *reinterpret_cast<uint16_t*>(bt + ((x.s.lq - 1) - step_row0(x, t)) * Sh::BT::PITCH +
                                        ((x.s.lk - 1) - x.kt * KT) * 2) = last;
         }
         __syncthreads();
@@ -308,7 +320,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // (left to the compiler, the row statistics and bias are read after them,
   // each waited for on its own); with LOAD the next unit's K fragments load
   // right after the S MFMAs, their last use ----
-  auto p_step = [&](auto load_tag, int u, int t, int st, f32x16* acc) __attribute__((always_inline)) {
+  auto p_step = [&](auto load_tag, const Unit& x, int u, int t, int st, f32x16* acc) __attribute__((always_inline)) {
     constexpr bool LOAD = decltype(load_tag)::value;
     const char* qt = smem + st * Sh::STAGE;
     bf16x8 fr[NKK];
@@ -340,6 +352,18 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const float lse = l4[i / 4][i % 4];
       const float c = BIAS ? fmaf((float)bv[i / 8][i % 8], kLog2e, -lse) : -lse;
       p[i] = fast_exp2(fmaf(sacc[i], A_scale_log2, c));
+    }
+    if constexpr (WIN) {
+      // P of pairs outside the window (and of rows or keys past the sample)
+      // is zero; the dS wave's dS = P (dP - Di) then is too.  A uniform
+      // branch skips the test for blocks wholly inside the window.
+      const int rbase = step_row0(x, t) + g * 4;
+      const int key = x.kt * KT + wv * 32 + l32;
+      const Window w{A_win_l, A_win_r, x.s.lq, x.s.lk};
+      if (!w.full(step_row0(x, t), x.kt * KT + wv * 32)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = w.allows(rbase + (i >> 2) * 8 + (i & 3), key) ? p[i] : 0.0f;
+      }
     }
     char* rec = px + (t & 1) * Sh::KB * Sh::PREC;
 #pragma unroll
@@ -451,22 +475,22 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       patch_tail(x, 0, cs);
       if (role == 0) {
         if (x.n == 1) {
-          p_step(std::true_type{}, u, 0, cs, acc);
+          p_step(std::true_type{}, x, u, 0, cs, acc);
           cs = next_stage(cs);
         } else {
-          p_step(std::false_type{}, u, 0, cs, acc);
+          p_step(std::false_type{}, x, u, 0, cs, acc);
           cs = next_stage(cs);
           for (int t = 1; t + 1 < x.n; ++t) {
             acquire();
             produce();
             patch_tail(x, t, cs);
-            p_step(std::false_type{}, u, t, cs, acc);
+            p_step(std::false_type{}, x, u, t, cs, acc);
             cs = next_stage(cs);
           }
           acquire();
           produce();
           patch_tail(x, x.n - 1, cs);
-          p_step(std::true_type{}, u, x.n - 1, cs, acc);
+          p_step(std::true_type{}, x, u, x.n - 1, cs, acc);
           cs = next_stage(cs);
         }
         // the partner reads P of the unit's last step after this barrier
