@@ -18,12 +18,19 @@ hipError_t dkdv2_one(const BwdArgs& a, int grid, hipStream_t st) {
                      a);
   return hipGetLastError();
 }
-// sliding window: 128-key units, 32-query steps, no dBias
+// sliding window: 128-key units, 32-query steps, no dBias (softmax without
+// split operands at D = 128 runs the wave-pair kernel: not instantiated here)
 template <int ACT>
 hipError_t dkdv2_window(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.wkv != 4 || k.dbias) return hipErrorInvalidValue;
-  if (k.bias) return k.split ? dkdv2_one<J_D, 4, 1, ACT, true, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, true, 0, false, true>(a, grid, st);
-  return k.split ? dkdv2_one<J_D, 4, 1, ACT, false, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, false, 0, false, true>(a, grid, st);
+  if constexpr (J_D == 128 && ACT == kSoftmax) {
+    if (!k.split) return hipErrorInvalidValue;
+    if (k.bias) return dkdv2_one<J_D, 4, 1, ACT, true, 0, true, true>(a, grid, st);
+    return dkdv2_one<J_D, 4, 1, ACT, false, 0, true, true>(a, grid, st);
+  } else {
+    if (k.bias) return k.split ? dkdv2_one<J_D, 4, 1, ACT, true, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, true, 0, false, true>(a, grid, st);
+    return k.split ? dkdv2_one<J_D, 4, 1, ACT, false, 0, true, true>(a, grid, st) : dkdv2_one<J_D, 4, 1, ACT, false, 0, false, true>(a, grid, st);
+  }
 }
 
 template <int D, int WKV, int WKQ, int ACT, bool SPLIT>
@@ -39,7 +46,10 @@ hipError_t dkdv2_bias(const BwdArgs& a, const KernelSel& k, int grid, hipStream_
 template <int D, int WKV, int WKQ, int ACT>
 hipError_t dkdv2_act(const BwdArgs& a, const KernelSel& k, int grid, hipStream_t st) {
   if (k.split) return dkdv2_bias<D, WKV, WKQ, ACT, true>(a, k, grid, st);
-  return dkdv2_bias<D, WKV, WKQ, ACT, false>(a, k, grid, st);
+  // softmax without split operands on 128-key units at D = 128 runs the
+  // wave-pair kernel: not instantiated here
+  if constexpr (D == 128 && WKV == 4 && ACT == kSoftmax) return hipErrorInvalidValue;
+  else return dkdv2_bias<D, WKV, WKQ, ACT, false>(a, k, grid, st);
 }
 
 template <int D, int WKV, int WKQ>
