@@ -1,4 +1,6 @@
-// dK/dV kernel of jagged attention for bf16 inputs, gfx950 (dense mask).
+// dK/dV kernel of jagged attention for bf16 inputs, gfx950, one wave per key
+// block (softmax without split operands on 128-key units at D = 128 runs the
+// wave-pair kernel instead: bwd_pair_impl.hpp).
 //
 // Method: "Training GEM at LLM scale" (Meta engineering post), section
 // "Jagged Sequence Flash Attention", item "Backward parallelization": dK and

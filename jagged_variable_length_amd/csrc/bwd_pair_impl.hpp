@@ -1,5 +1,5 @@
-// dK/dV kernel with a wave pair per key block: bf16 inputs, softmax, dense
-// mask, gfx950.
+// dK/dV kernel with a wave pair per key block: bf16 inputs, softmax over a
+// dense mask or a sliding window, 128-key units, gfx950.
 //
 // Method: "Training GEM at LLM scale" (Meta engineering post), section
 // "Jagged Sequence Flash Attention", item "Backward parallelization": dK and
@@ -23,8 +23,9 @@
 // query rows), so the hand-over is a lane-private 64-byte record per lane
 // (fp32, so that dS is formed from P before its rounding to the bf16 MFMA
 // operand, as in the single-wave kernel).
-// The dS wave's MFMAs for dP of step t are interleaved with its VALU work on
-// dS of step t - 1.
+// The dS wave's MFMAs for dP of step t are written interleaved with its VALU
+// work on dS of step t - 1 (with dBias its stores hold that order; without
+// them the compiler may issue the MFMAs first).
 //
 // Sliding window (WIN, section "BlockAttention"): a unit's steps start at the
 // first query block whose window reaches its keys; the P wave zeroes P

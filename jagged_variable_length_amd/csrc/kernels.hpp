@@ -176,7 +176,8 @@ hipError_t launch_dkdv2_64_bf16(const BwdArgs&, const KernelSel&, int, hipStream
 hipError_t launch_dkdv2_64_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
 hipError_t launch_dkdv2_32_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
 hipError_t launch_dkdv2_32_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
-// wave-pair dK/dV (bf16 inputs, softmax, dense mask, 128-key units)
+// wave-pair dK/dV (bf16 inputs, softmax without split operands, dense mask or
+// sliding window, 128-key units, D = 128)
 hipError_t launch_dkdv_pair_128_bf16(const BwdArgs&, const KernelSel&, int, hipStream_t);
 hipError_t launch_dkdv_pair_128_f32(const BwdArgs&, const KernelSel&, int, hipStream_t);
 
