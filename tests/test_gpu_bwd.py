@@ -84,6 +84,25 @@ def test_bwd_gdpa_bias_long_queries(act):
     _compare(inp, op, got)
 
 
+@pytest.mark.parametrize("D", [64, 32])
+@pytest.mark.parametrize("act", ["softmax", "silu", "gelu"])
+def test_bwd_two_workgroups_per_cu(D, act):
+    """dK/dV at D <= 64 without a bias on 64-key units runs two workgroups per
+    CU over twice the workers; erf-GELU keeps one (its registers do not fit
+    two waves per SIMD).  The plan's dK/dV worker count shows which ran."""
+    say(f"case: bwd two dK/dV workgroups per CU D={D} act={act}")
+    rng = np.random.default_rng(D + len(act))
+    lk = rng.integers(33, 65, 12)  # mean key count in (32, 64]: 64-key units
+    lq = rng.integers(0, 400, 12)
+    inp = gen.make_custom(lq, lk, 2, D, "bf16", seed=D + len(act))
+    gdpa = act != "softmax"
+    op, got, _ = _run(inp, act=act, split=gdpa, out_dtype="f32" if gdpa else None, grad_dtype="f32",
+                      num_workers=64)
+    assert op.info.dkdv.tile_rows == 64
+    assert op.info.dkdv.num_workers == (64 if act == "gelu" else 128)
+    _compare(inp, op, got)
+
+
 @pytest.mark.parametrize("D,bias,tile", [(64, True, 32), (128, False, 32), (128, True, 256)])
 def test_bwd_short_query_softmax(D, bias, tile):
     """Short query tiles: the dQ kernel splits each 32-row group's keys over
