@@ -281,8 +281,17 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
       if (p->dq_wq == 4) p->dq_wq = 8;
     }
     if (d.mask == JATTN_MASK_WINDOW) p->fwd_wq = p->dq_wq = 4;
+    // bf16 forward at D <= 64 without a bias or window, long queries: 4 query
+    // groups over one 32-key block per step, three workgroups per CU (the
+    // kernel's ~160 registers fit three waves per SIMD), over three times the
+    // workers (fwd2_waves_per_simd applies the same rule).  dQ keeps 8 x 1:
+    // the same shape there measured slower (its K/V stages serve half the
+    // query rows)
+    const bool fwd_three = d.in_dtype == JATTN_BF16 && d.D <= 64 && !d.has_bias && d.mask == JATTN_MASK_NONE &&
+                           p->fwd_wq == 8;
+    if (fwd_three) p->fwd_wq = 4;
     auto step_of = [](int wq) { return wq == 8 ? 32 : wq == 4 ? 64 : 128; };
-    const int fwd_tile = 32 * p->fwd_wq, fwd_step = step_of(p->fwd_wq);
+    const int fwd_tile = 32 * p->fwd_wq, fwd_step = fwd_three ? 32 : step_of(p->fwd_wq);
     const int dq_tile = 32 * p->dq_wq, dq_step = step_of(p->dq_wq);
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
@@ -294,7 +303,7 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     jattn::Window win;
     win.left = p->win_l;
     win.right = p->win_r;
-    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, W, order, &p->fwd, win);
+    jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, fwd_three ? 3 * W : W, order, &p->fwd, win);
     jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, W, order, &p->dq, win);
     // the bf16 dK/dV kernel runs two workgroups per CU at D <= 64 without a
     // bias or window on 64- or 128-key units (not with erf-GELU): twice the

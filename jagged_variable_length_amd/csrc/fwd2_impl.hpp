@@ -82,8 +82,16 @@ struct Fwd2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
+// 4 query groups x one key block at D <= 64 without a bias or window run
+// three workgroups per CU (the plan gives that shape three times the
+// workers); the other shapes keep the default (at least one)
+template <int D, int WQ, int WK, bool BIAS, bool WIN>
+constexpr int fwd2_waves_per_simd() {
+  return D <= 64 && WQ == 4 && WK == 1 && !BIAS && !WIN ? 3 : 1;
+}
+
 template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>
-__global__ __launch_bounds__(64 * WQ * WK, 1) void fwd2_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * WQ * WK, (fwd2_waves_per_simd<D, WQ, WK, BIAS, WIN>())) void fwd2_kernel(FwdArgs a) {
   using Sh = Fwd2Shape<D, WQ, WK, BIAS>;
   constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW, NS = Sh::NS;
   // software pipeline across steps when the ring holds three stages or more

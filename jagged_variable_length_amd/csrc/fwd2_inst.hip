@@ -69,6 +69,17 @@ hipError_t dispatch(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t 
   // quarters (128-key steps) for short queries (4 x 2 serves the windowed
   // instances above)
   if (k.wq == 8) return shape<TO, 8, 1>(a, k, grid, st);
+  if constexpr (J_D <= 64) {
+    // 4 query groups over one 32-key block per step, three workgroups per CU
+    // (no bias)
+    if (k.wq == 4) {
+      if (k.bias) return hipErrorInvalidValue;
+      if (k.act == kSoftmax) return one<TO, 4, 1, kSoftmax, false, false>(a, grid, st);
+      if (k.act == kGelu) return k.split ? one<TO, 4, 1, kGelu, false, true>(a, grid, st) : one<TO, 4, 1, kGelu, false, false>(a, grid, st);
+      if (k.act == kGeluPoly) return k.split ? one<TO, 4, 1, kGeluPoly, false, true>(a, grid, st) : one<TO, 4, 1, kGeluPoly, false, false>(a, grid, st);
+      return k.split ? one<TO, 4, 1, kSilu, false, true>(a, grid, st) : one<TO, 4, 1, kSilu, false, false>(a, grid, st);
+    }
+  }
   if (k.wq != 1) return hipErrorInvalidValue;
   if constexpr (J_D == 128) {
     // short queries with bias at D = 128 do not fit the LDS budget; the

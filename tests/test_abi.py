@@ -239,9 +239,17 @@ def test_random_plans_match(lib, seed):
             for kind, which, kp in parts:
                 units = B.jattn_plan_export(p, which * 2).reshape(-1, 4)
                 offs = B.jattn_plan_export(p, which * 2 + 1)
-                # the plan's own worker count of the pass (dK/dV at D = 64 without a
-                # bias runs two workgroups per CU over twice the workers asked for)
-                assert kp.num_workers in (W, 2 * W)
+                # the plan's own worker count of the pass: dK/dV at D = 64 without a
+                # bias runs two workgroups per CU over twice the workers asked for;
+                # the forward with 128-row tiles and 32-key steps three over three
+                # times as many
+                if kind == "dkdv":
+                    assert kp.num_workers in (W, 2 * W)
+                elif kind == "fwd":
+                    three = (kp.tile_rows, kp.step_rows) == (128, 32)
+                    assert kp.num_workers == (3 * W if three else W)
+                else:
+                    assert kp.num_workers == W
                 ref_u, ref_o = P.plan(kind, lq.tolist(), lk.tolist(), 3, kp.tile_rows, kp.step_rows,
                                       kp.num_workers, ["heavy_first", "zigzag", "lpt"][order])
                 np.testing.assert_array_equal(units, np.array(ref_u, np.int32).reshape(-1, 4))

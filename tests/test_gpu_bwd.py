@@ -8,7 +8,7 @@ from jagged_variable_length_amd import inputs as gen
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check, check_dbias, device_inputs, make_op, oracle_bwd, say, sync  # noqa: E402
+from gpu_util import check, check_dbias, check_lse, device_inputs, make_op, oracle_bwd, oracle_fwd, say, sync  # noqa: E402
 
 
 def _run(inp, **kw):
@@ -100,6 +100,42 @@ def test_bwd_two_workgroups_per_cu(D, act):
                       num_workers=64)
     assert op.info.dkdv.tile_rows == 64
     assert op.info.dkdv.num_workers == (64 if act == "gelu" else 128)
+    _compare(inp, op, got)
+
+
+@pytest.mark.parametrize("D,act,split,out", [
+    (64, "softmax", False, "bf16"), (32, "softmax", False, "f32"),
+    (64, "softmax", True, "f32"),
+    (64, "gelu", True, "f32"), (32, "silu", True, "f32"), (64, "gelu_poly", True, "f32"),
+    (32, "gelu_poly", True, "bf16")])
+def test_fwd_three_workgroups_per_cu(D, act, split, out):
+    """The bf16 forward at D <= 64 without a bias or window on long queries
+    takes 128-row tiles with 32-key steps, three workgroups per CU, over three
+    times the workers (dQ keeps 256-row tiles); the plan's tile shapes and
+    worker counts show which ran.  The whole backward is checked after it."""
+    say(f"case: fwd three workgroups per CU D={D} act={act} split={split} out={out}")
+    rng = np.random.default_rng(D + 7 * len(act) + split)
+    lq = rng.integers(60, 400, 10)
+    lq[3] = 0
+    # at least 33 keys a sample (one full step and a ragged one); a one-key
+    # sample (P = 1, where the rounding of O in Di reaches dS undamped and adds
+    # up over a key's queries) only with fp32 O
+    lk = rng.integers(33, 120, 10)
+    lk[6] = 0
+    if out == "f32":
+        lk[8] = 1
+    inp = gen.make_custom(lq, lk, 2, D, "bf16", seed=D + len(act) + split)
+    if act == "gelu_poly":
+        # its polynomial tanh is meant for small scores (QK-normalised rows):
+        # Q / 4, exact in bf16, keeps |s| near 1
+        inp.q = gen.f32_to_bf16_bits((inp.f64("q") * 0.25).astype(np.float32))
+    op, got, (o, lse, _) = _run(inp, act=act, split=split, out_dtype=out, grad_dtype="f32", num_workers=64)
+    assert (op.info.fwd.tile_rows, op.info.fwd.step_rows, op.info.fwd.num_workers) == (128, 32, 192)
+    assert (op.info.dq.tile_rows, op.info.dq.step_rows, op.info.dq.num_workers) == (256, 32, 64)
+    ref_o, ref_lse = oracle_fwd(inp, op)
+    check(A.to_f64(o), ref_o, "O")
+    if act == "softmax":
+        check_lse(A.to_f64(lse), ref_lse)
     _compare(inp, op, got)
 
 
