@@ -322,7 +322,7 @@ def host_info():
 
 
 class ClockSampler:
-    """Samples the shader clock the driver reports (the active level of
+    """Samples the shader clock the amdgpu kernel driver reports (the active level of
     pp_dpm_sclk of the card in use) while the timed steps run."""
 
     def __init__(self, torch):
