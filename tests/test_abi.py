@@ -258,6 +258,43 @@ def test_random_plans_match(lib, seed):
             B.jattn_plan_destroy(p)
 
 
+_LONG_Q = [300, 200, 100]
+
+
+@pytest.mark.parametrize("kw,lq,lk,fwd,dkdv", [
+    # bf16 at D <= 64 without bias or window, long queries: the forward on
+    # 128-row tiles with 32-key steps over 3x the workers; dK/dV on 128-key
+    # tiles with two workgroups per CU over 2x
+    (dict(D=64), _LONG_Q, [100, 90, 80], (128, 32, 48), (128, 32)),
+    (dict(D=32), _LONG_Q, [100, 90, 80], (128, 32, 48), (128, 32)),
+    (dict(D=64, act=B.JATTN_SILU), _LONG_Q, [100, 90, 80], (128, 32, 48), (128, 32)),
+    # erf-GELU keeps one dK/dV workgroup per CU (the forward rule holds)
+    (dict(D=64, act=B.JATTN_GELU_ERF), _LONG_Q, [100, 90, 80], (128, 32, 48), (128, 16)),
+    # 32-key dK/dV tiles (mean lk <= 32) keep one
+    (dict(D=64), _LONG_Q, [20, 30, 10], (128, 32, 48), (32, 16)),
+    # D = 128, a bias, fp32 inputs, a window or short queries: neither rule
+    (dict(D=128), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
+    (dict(D=64, has_bias=1), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
+    (dict(D=64, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32), _LONG_Q, [100, 90, 80],
+     (128, 64, 16), (128, 16)),
+    (dict(D=64, mask=B.JATTN_MASK_WINDOW, window=(40, 7)), _LONG_Q, _LONG_Q, (128, 64, 16), (128, 16)),
+    (dict(D=64), [20, 30, 10], [100, 90, 80], (32, 128, 16), (128, 32)),
+])
+def test_plan_occupancy_rules(lib, kw, lq, lk, fwd, dkdv):
+    """Tile shape and worker count of the forward, and key tile and worker
+    count of dK/dV, on each side of the rules that run two or three
+    workgroups per CU (host only: plan creation makes no GPU call)."""
+    d = _desc(B=len(lq), num_workers=16, **kw)
+    p = B.jattn_plan_create(d, gen.offsets_from_lengths(np.array(lq)), gen.offsets_from_lengths(np.array(lk)))
+    try:
+        info = B.jattn_plan_info(p)
+        assert (info.fwd.tile_rows, info.fwd.step_rows, info.fwd.num_workers) == fwd
+        assert (info.dkdv.tile_rows, info.dkdv.num_workers) == dkdv
+        assert info.dq.num_workers == 16  # dQ never multiplies its workers
+    finally:
+        B.jattn_plan_destroy(p)
+
+
 def test_empty_batch_plans(lib):
     d = _desc(B=0)
     p = B.jattn_plan_create(d, [0], [0])
