@@ -138,9 +138,10 @@ typedef struct {
                            bf16 dK/dV pass at D <= 64 without bias or window
                            on 64- or 128-key tiles (not erf-GELU) runs two
                            workgroups per CU and is planned over twice this
-                           number; the bf16 forward at D <= 64 without bias
-                           or window on 128-row query tiles runs three and is
-                           planned over three times it
+                           number; the bf16 forward without bias or window
+                           on 128-row query tiles runs three at D <= 64 and
+                           (softmax) two at D = 128, planned over three or
+                           two times it
                            (jattn_plan_summary reports each pass's) */
   int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
   int32_t window_left;  /* JATTN_MASK_WINDOW: keys before the query it sees (>= 0) */

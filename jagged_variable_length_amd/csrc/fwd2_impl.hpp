@@ -82,12 +82,13 @@ struct Fwd2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-// 4 query groups x one key block at D <= 64 without a bias or window run
-// three workgroups per CU (the plan gives that shape three times the
-// workers); the other shapes keep the default (at least one)
+// 4 query groups x one key block without a bias or window run three
+// workgroups per CU at D <= 64 and two at D = 128 (the plan gives that shape
+// three or two times the workers); the other shapes keep the default (at
+// least one)
 template <int D, int WQ, int WK, bool BIAS, bool WIN>
 constexpr int fwd2_waves_per_simd() {
-  return D <= 64 && WQ == 4 && WK == 1 && !BIAS && !WIN ? 3 : 1;
+  return WQ == 4 && WK == 1 && !BIAS && !WIN ? (D <= 64 ? 3 : 2) : 1;
 }
 
 template <typename TO, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false>

@@ -69,7 +69,14 @@ hipError_t dispatch(const FwdArgs& a, const KernelSel& k, int grid, hipStream_t 
   // quarters (128-key steps) for short queries (4 x 2 serves the windowed
   // instances above)
   if (k.wq == 8) return shape<TO, 8, 1>(a, k, grid, st);
-  if constexpr (J_D <= 64) {
+  if constexpr (J_D == 128) {
+    // 4 query groups over one 32-key block per step, two workgroups per CU
+    // (softmax, no bias)
+    if (k.wq == 4) {
+      if (k.bias || k.act != kSoftmax) return hipErrorInvalidValue;
+      return one<TO, 4, 1, kSoftmax, false, false>(a, grid, st);
+    }
+  } else {
     // 4 query groups over one 32-key block per step, three workgroups per CU
     // (no bias)
     if (k.wq == 4) {

@@ -241,8 +241,8 @@ def test_random_plans_match(lib, seed):
                 offs = B.jattn_plan_export(p, which * 2 + 1)
                 # the plan's own worker count of the pass: dK/dV at D = 64 without a
                 # bias runs two workgroups per CU over twice the workers asked for;
-                # the forward with 128-row tiles and 32-key steps three over three
-                # times as many
+                # the forward at D = 64 with 128-row tiles and 32-key steps three
+                # over three times as many
                 if kind == "dkdv":
                     assert kp.num_workers in (W, 2 * W)
                 elif kind == "fwd":
@@ -272,8 +272,12 @@ _LONG_Q = [300, 200, 100]
     (dict(D=64, act=B.JATTN_GELU_ERF), _LONG_Q, [100, 90, 80], (128, 32, 48), (128, 16)),
     # 32-key dK/dV tiles (mean lk <= 32) keep one
     (dict(D=64), _LONG_Q, [20, 30, 10], (128, 32, 48), (32, 16)),
-    # D = 128, a bias, fp32 inputs, a window or short queries: neither rule
-    (dict(D=128), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
+    # D = 128 softmax without bias or window: the forward's 128 x 32 tiles run
+    # two workgroups per CU over 2x the workers (GDPA keeps 256 x 32)
+    (dict(D=128), _LONG_Q, [100, 90, 80], (128, 32, 32), (128, 16)),
+    (dict(D=128, act=B.JATTN_GELU_ERF), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
+    # a bias, fp32 inputs, a window or short queries: neither rule
+    (dict(D=128, has_bias=1), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
     (dict(D=64, has_bias=1), _LONG_Q, [100, 90, 80], (256, 32, 16), (128, 16)),
     (dict(D=64, in_dtype=B.JATTN_F32, out_dtype=B.JATTN_F32, grad_dtype=B.JATTN_F32), _LONG_Q, [100, 90, 80],
      (128, 64, 16), (128, 16)),

@@ -140,6 +140,27 @@ def test_fwd_three_workgroups_per_cu(D, act, split, out, W):
     _compare(inp, op, got)
 
 
+@pytest.mark.parametrize("W,out", [(64, "bf16"), (7, "f32")])
+def test_fwd_two_workgroups_per_cu_d128(W, out):
+    """The bf16 softmax forward at D = 128 without a bias or window takes
+    128-row tiles with 32-key steps, two workgroups per CU, over twice the
+    workers (7 asked for: 14, not a multiple of the 8 XCDs); the whole
+    backward is checked after it."""
+    say(f"case: fwd two workgroups per CU D=128 W={W} out={out}")
+    rng = np.random.default_rng(128 + W)
+    lq = rng.integers(60, 500, 10)
+    lq[2] = 0
+    lk = rng.integers(33, 400, 10)
+    lk[5] = 0
+    inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=128 + W)
+    op, got, (o, lse, _) = _run(inp, out_dtype=out, grad_dtype="f32", num_workers=W)
+    assert (op.info.fwd.tile_rows, op.info.fwd.step_rows, op.info.fwd.num_workers) == (128, 32, 2 * W)
+    ref_o, ref_lse = oracle_fwd(inp, op)
+    check(A.to_f64(o), ref_o, "O")
+    check_lse(A.to_f64(lse), ref_lse)
+    _compare(inp, op, got)
+
+
 @pytest.mark.parametrize("D,bias,tile", [(64, True, 32), (128, False, 32), (128, True, 256)])
 def test_bwd_short_query_softmax(D, bias, tile):
     """Short query tiles: the dQ kernel splits each 32-row group's keys over
