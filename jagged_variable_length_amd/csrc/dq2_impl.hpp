@@ -72,11 +72,19 @@ struct Dq2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
+// 4 query groups x one key block at D = 128 without a bias or window run two
+// workgroups per CU (the plan gives that shape twice the workers); the other
+// shapes keep the default (at least one)
+template <int D, int WQ, int WK, bool BIAS, bool WIN>
+constexpr int dq2_waves_per_simd() {
+  return D == 128 && WQ == 4 && WK == 1 && !BIAS && !WIN ? 2 : 1;
+}
+
 // OF (softmax only): 0 = Di and LSE*log2e read from the workspace; 1 / 2 =
 // formed here from O (bf16 / fp32), dO and the natural LSE, and written to
 // the workspace for the dK/dV pass, which then runs after this one.
 template <typename TG, int D, int WQ, int WK, int ACT, bool BIAS, bool SPLIT, bool WIN = false, int OF = 0>
-__global__ __launch_bounds__(64 * WQ * WK, 1) void dq2_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * WQ * WK, (dq2_waves_per_simd<D, WQ, WK, BIAS, WIN>())) void dq2_kernel(BwdArgs a) {
   using Sh = Dq2Shape<D, WQ, WK, BIAS>;
   constexpr int BM = Sh::BM, BN = Sh::BN, ND = Sh::ND, NKK = Sh::NKK, NW = Sh::NW, NS = Sh::NS;
   constexpr bool SOFTMAX = (ACT == kSoftmax);

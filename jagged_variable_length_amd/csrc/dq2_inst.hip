@@ -79,6 +79,14 @@ hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int g
     return dq2_window<kSilu>(a, k, grid, st);
   }
   if (k.wq == 8) return dq2_shape<8, 1>(a, k, grid, st);
+  if constexpr (J_D == 128) {
+    // 4 query groups over one 32-key block per step, two workgroups per CU
+    // (softmax without a bias or split operands)
+    if (k.wq == 4) {
+      if (k.bias || k.split || k.act != kSoftmax) return hipErrorInvalidValue;
+      return dq2_one<4, 1, kSoftmax, false, false>(a, k, grid, st);
+    }
+  }
   if (k.wq != 1) return hipErrorInvalidValue;  // 4 x 2 serves the windowed instances only
   return dq2_shape<1, 4>(a, k, grid, st);
 }

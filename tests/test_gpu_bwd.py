@@ -142,8 +142,8 @@ def test_fwd_three_workgroups_per_cu(D, act, split, out, W):
 
 @pytest.mark.parametrize("W,out", [(64, "bf16"), (7, "f32")])
 def test_fwd_two_workgroups_per_cu_d128(W, out):
-    """The bf16 softmax forward at D = 128 without a bias or window takes
-    128-row tiles with 32-key steps, two workgroups per CU, over twice the
+    """The bf16 softmax forward and dQ at D = 128 without a bias or window
+    take 128-row tiles with 32-key steps, two workgroups per CU, over twice the
     workers (7 asked for: 14, not a multiple of the 8 XCDs); the whole
     backward is checked after it."""
     say(f"case: fwd two workgroups per CU D=128 W={W} out={out}")
@@ -155,6 +155,8 @@ def test_fwd_two_workgroups_per_cu_d128(W, out):
     inp = gen.make_custom(lq, lk, 2, 128, "bf16", seed=128 + W)
     op, got, (o, lse, _) = _run(inp, out_dtype=out, grad_dtype="f32", num_workers=W)
     assert (op.info.fwd.tile_rows, op.info.fwd.step_rows, op.info.fwd.num_workers) == (128, 32, 2 * W)
+    # dQ takes the same tile shape, also two workgroups per CU
+    assert (op.info.dq.tile_rows, op.info.dq.step_rows, op.info.dq.num_workers) == (128, 32, 2 * W)
     ref_o, ref_lse = oracle_fwd(inp, op)
     check(A.to_f64(o), ref_o, "O")
     check_lse(A.to_f64(lse), ref_lse)
