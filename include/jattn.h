@@ -141,9 +141,9 @@ typedef struct {
                            number; the bf16 forward without bias or window
                            on 128-row query tiles runs three at D <= 64 and
                            (softmax) two at D = 128, planned over three or
-                           two times it; so does the bf16 softmax dQ pass at
-                           D = 128 without bias, window or split operands
-                           (two, over twice it)
+                           two times it; the bf16 softmax dQ pass without
+                           bias or window (at D = 128 also without split
+                           operands) runs two, over twice it
                            (jattn_plan_summary reports each pass's) */
   int32_t dbias_dtype;  /* dbias: JATTN_BF16 | JATTN_F32 */
   int32_t window_left;  /* JATTN_MASK_WINDOW: keys before the query it sees (>= 0) */

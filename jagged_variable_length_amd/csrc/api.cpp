@@ -298,13 +298,16 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     if (fwd_two) p->fwd_wq = 4;
     // dQ at D = 128 (softmax without a bias, window or split operands): the
     // same 128-row tiles over 32-key steps, two workgroups per CU over twice
-    // the workers
+    // the workers; at D <= 64 (softmax without a bias or window, split
+    // operands allowed) the same
     const bool dq_two = d.in_dtype == JATTN_BF16 && d.D == 128 && !d.has_bias && d.mask == JATTN_MASK_NONE &&
                         d.act == JATTN_SOFTMAX && !d.split_operands && p->dq_wq == 8;
-    if (dq_two) p->dq_wq = 4;
+    const bool dq_two64 = d.in_dtype == JATTN_BF16 && d.D <= 64 && !d.has_bias && d.mask == JATTN_MASK_NONE &&
+                          d.act == JATTN_SOFTMAX && p->dq_wq == 8;
+    if (dq_two || dq_two64) p->dq_wq = 4;
     auto step_of = [](int wq) { return wq == 8 ? 32 : wq == 4 ? 64 : 128; };
     const int fwd_tile = 32 * p->fwd_wq, fwd_step = (fwd_three || fwd_two) ? 32 : step_of(p->fwd_wq);
-    const int dq_tile = 32 * p->dq_wq, dq_step = dq_two ? 32 : step_of(p->dq_wq);
+    const int dq_tile = 32 * p->dq_wq, dq_step = (dq_two || dq_two64) ? 32 : step_of(p->dq_wq);
     // Key-tile shape of dK/dV: 32, 64 or 128 keys per unit.
     p->dkdv_wkv = (n_k > 0 && sum_lk <= 32 * n_k) ? 1 : (n_k > 0 && sum_lk <= 64 * n_k) ? 2 : 4;
     // the bf16 dK/dV kernel keeps three or four step stages in LDS: 128-query
@@ -316,7 +319,7 @@ int jattn_plan_create(const jattn_desc* desc, const int64_t* q_offsets, const in
     win.left = p->win_l;
     win.right = p->win_r;
     jattn::plan_units(jattn::kKindFwd, lq, lk, d.H, fwd_tile, fwd_step, fwd_three ? 3 * W : fwd_two ? 2 * W : W, order, &p->fwd, win);
-    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, dq_two ? 2 * W : W, order, &p->dq, win);
+    jattn::plan_units(jattn::kKindDq, lq, lk, d.H, dq_tile, dq_step, (dq_two || dq_two64) ? 2 * W : W, order, &p->dq, win);
     // the bf16 dK/dV kernel runs two workgroups per CU at D <= 64 without a
     // bias or window on 64- or 128-key units (not with erf-GELU): twice the
     // workers (the kernel's dkdv2_waves_per_simd applies the same rule)

@@ -72,12 +72,13 @@ struct Dq2Shape {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-// 4 query groups x one key block at D = 128 without a bias or window run two
-// workgroups per CU (the plan gives that shape twice the workers); the other
-// shapes keep the default (at least one)
+// 4 query groups x one key block without a bias or window run two
+// workgroups per CU (the plan gives that shape twice the workers; three at
+// D = 64 would spill the bf16-gradient instance that reads fp32 O); the
+// other shapes keep the default (at least one)
 template <int D, int WQ, int WK, bool BIAS, bool WIN>
 constexpr int dq2_waves_per_simd() {
-  return D == 128 && WQ == 4 && WK == 1 && !BIAS && !WIN ? 2 : 1;
+  return WQ == 4 && WK == 1 && !BIAS && !WIN ? 2 : 1;
 }
 
 // OF (softmax only): 0 = Di and LSE*log2e read from the workspace; 1 / 2 =

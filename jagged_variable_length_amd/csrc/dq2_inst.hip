@@ -86,6 +86,13 @@ hipError_t JATTN_DQ2_NAME(J_D, J_TG)(const BwdArgs& a, const KernelSel& k, int g
       if (k.bias || k.split || k.act != kSoftmax) return hipErrorInvalidValue;
       return dq2_one<4, 1, kSoftmax, false, false>(a, k, grid, st);
     }
+  } else {
+    // the same shape, two workgroups per CU (softmax without a bias)
+    if (k.wq == 4) {
+      if (k.bias || k.act != kSoftmax) return hipErrorInvalidValue;
+      if (k.split) return dq2_one<4, 1, kSoftmax, false, true>(a, k, grid, st);
+      return dq2_one<4, 1, kSoftmax, false, false>(a, k, grid, st);
+    }
   }
   if (k.wq != 1) return hipErrorInvalidValue;  // 4 x 2 serves the windowed instances only
   return dq2_shape<1, 4>(a, k, grid, st);
